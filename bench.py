@@ -1,0 +1,323 @@
+"""Benchmark of the FP8 scaled-GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-recipes] [--workload NAME]
+
+One step = one pass of the whole hot path over the workload's synthetic
+inputs (already resident in HBM): dynamic quantization of both operands
+(group amax -> scale -> saturating E4M3 cast) and the scaled GEMM with its
+scale application and bf16 epilogue.  The default workload is the blockwise
+1x128 x 128x128 forward GEMM at M=16640, N=5120, K=8192 (the shape the
+method's published blockwise table and its 60 %-of-peak target use).
+
+Printed: one JSON line with the step throughput (GEMM flops 2*M*N*K per step
+over the step time), the roofline of the dominant kernel (the GEMM, timed
+with HIP events on the stream it is launched on), per-recipe kernel-level
+numbers for every workload, and the CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP8_DENSE_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA (no sparsity)
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="blockwise_fwd_16640x5120x8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-recipes", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters (optional)")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# workloads: (name, builder) -> dict with 'step' (callable), 'flops',
+# 'gemm' (callable launching only the GEMM), 'gemm_bytes' (algorithmic)
+# --------------------------------------------------------------------------
+
+def _dev_bf16(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def build_workloads(torch, fp8mm, workloads):
+    W = {}
+
+    def blockwise_fwd(M, N, K):
+        inp = workloads.blockwise(M=M, N=N, K=K)
+        x, w = _dev_bf16(inp["input"], torch), _dev_bf16(inp["weight"], torch)
+        state = {}
+
+        def quant():
+            state["qx"], state["sx"] = fp8mm.fp8_quantize_blockwise(x, (1, 128))
+            state["qw"], state["sw"] = fp8mm.fp8_quantize_blockwise(w, (128, 128))
+
+        def gemm():
+            return fp8mm.fp8_scaled_mm(state["qx"], state["qw"], state["sx"], "1x128", state["sw"], "128x128")
+
+        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+                    gemm_bytes=M * K + N * K + 4 * (K // 128) * (M + N // 128) + 2 * M * N,
+                    quant_bytes=3 * (M * K + N * K) + 4 * ((K // 128) * M + (N // 128) * (K // 128)),
+                    shape=(M, N, K), recipe="blockwise_1x128_128x128")
+
+    def blockwise_grad_input(M, N, K):
+        # grad_input[M, K] = grad_output[M, N] @ weight[N, K]
+        inp = workloads.blockwise(M=M, N=N, K=K)
+        g, w = _dev_bf16(inp["grad_output"], torch), _dev_bf16(inp["weight"], torch)
+        state = {}
+
+        def quant():
+            state["qg"], state["sg"] = fp8mm.fp8_quantize_blockwise(g, (1, 128))
+            state["qw"], state["sw"] = fp8mm.fp8_quantize_blockwise(w, (128, 128))
+
+        def gemm():
+            return fp8mm.fp8_linear_grad_input(state["qg"], state["sg"], "1x128", state["qw"], state["sw"], "128x128")
+
+        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+                    gemm_bytes=M * N + N * K + 4 * (N // 128) * (M + K // 128) + 2 * M * K,
+                    quant_bytes=3 * (M * N + N * K), shape=(M, K, N), recipe="blockwise_1x128_128x128 (KN)")
+
+    def blockwise_grad_weight(T, N_out, K_in):
+        inp = workloads.grad_weight(T=T, N_out=N_out, K_in=K_in)
+        g, x = _dev_bf16(inp["grad_output"], torch), _dev_bf16(inp["input"], torch)
+        state = {}
+
+        def quant():
+            state["qg"], state["sg"] = fp8mm.fp8_quantize_blockwise(g, (128, 1), transpose_out=True)
+            state["qx"], state["sx"] = fp8mm.fp8_quantize_blockwise(x, (128, 1), transpose_out=True)
+
+        def gemm():
+            return fp8mm.fp8_linear_grad_weight(state["qg"], state["sg"], state["qx"], state["sx"])
+
+        return dict(quant=quant, gemm=gemm, flops=2.0 * T * N_out * K_in,
+                    gemm_bytes=T * (N_out + K_in) + 4 * (T // 128) * (N_out + K_in) + 2 * N_out * K_in,
+                    quant_bytes=3 * T * (N_out + K_in), shape=(N_out, K_in, T), recipe="blockwise_1x128_128x1")
+
+    def rowwise(M, N, K):
+        inp = workloads.rowwise(M=M, N=N, K=K)
+        x, w, b = _dev_bf16(inp["x"], torch), _dev_bf16(inp["w"], torch), _dev_bf16(inp["bias"], torch)
+        state = {}
+
+        def quant():
+            state["qx"], state["sx"] = fp8mm.fp8_quantize_rowwise(x)
+            state["qw"], state["sw"] = fp8mm.fp8_quantize_rowwise(w)
+
+        def gemm():
+            return fp8mm.fp8_scaled_mm(state["qx"], state["qw"], state["sx"], "rowwise", state["sw"], "rowwise", bias=b)
+
+        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+                    gemm_bytes=M * K + N * K + 4 * (M + N) + 2 * N + 2 * M * N,
+                    quant_bytes=3 * (M * K + N * K) + 4 * (M + N), shape=(M, N, K), recipe="rowwise_rowwise")
+
+    def tensorwise(n):
+        inp = workloads.tensorwise(n=n)
+        a, b = _dev_bf16(inp["A"], torch), _dev_bf16(inp["B"], torch)
+        state = {}
+
+        def quant():
+            state["qa"], state["sa"] = fp8mm.fp8_quantize_tensorwise(a)
+            state["qb"], state["sb"] = fp8mm.fp8_quantize_tensorwise(b)
+
+        def gemm():
+            return fp8mm.fp8_scaled_mm(state["qa"], state["qb"], state["sa"], "tensorwise", state["sb"], "tensorwise")
+
+        return dict(quant=quant, gemm=gemm, flops=2.0 * n ** 3, gemm_bytes=2 * n * n + 8 + 2 * n * n,
+                    quant_bytes=6 * n * n, shape=(n, n, n), recipe="tensorwise_tensorwise")
+
+    def grouped():
+        inp = workloads.grouped()
+        act = _dev_bf16(inp["act"], torch)
+        E, N, K = inp["W"].shape
+        Wd = _dev_bf16(inp["W"].reshape(E * N, K), torch)
+        offs = torch.from_numpy(inp["offs"]).cuda()
+        M = int(inp["offs"][-1])
+        state = {}
+
+        def quant():
+            state["qa"], state["sa"] = fp8mm.fp8_quantize_rowwise(act)
+            state["qw"], state["sw"] = fp8mm.fp8_quantize_rowwise(Wd)
+
+        def gemm():
+            return fp8mm.fp8_scaled_grouped_mm(state["qa"], state["qw"].view(E, N, K), offs, state["sa"],
+                                               state["sw"].view(E, N))
+
+        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+                    gemm_bytes=M * K + E * N * K + 4 * (M + E * N) + 4 * E + 2 * M * N,
+                    quant_bytes=3 * (M * K + E * N * K) + 4 * (M + E * N), shape=(M, N, K, E),
+                    recipe="grouped_rowwise_E64")
+
+    W["tensorwise_256"] = lambda: tensorwise(256)
+    W["rowwise_8192x4096x4096"] = lambda: rowwise(8192, 4096, 4096)
+    W["blockwise_fwd_16640x5120x8192"] = lambda: blockwise_fwd(16640, 5120, 8192)
+    W["blockwise_fwd_16640x8192x5120"] = lambda: blockwise_fwd(16640, 8192, 5120)
+    W["blockwise_grad_input_16640x8192x5120"] = lambda: blockwise_grad_input(16640, 5120, 8192)
+    W["blockwise_grad_input_16640x5120x8192"] = lambda: blockwise_grad_input(16640, 8192, 5120)
+    W["blockwise_grad_weight_5120x8192x16640"] = lambda: blockwise_grad_weight(16640, 5120, 8192)
+    W["grouped_moe_E64_16384x1408x2048"] = grouped
+    return W
+
+
+def time_kernel(torch, fn, iters, warmup=3):
+    """Median device time (ms) of fn's launches, HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    evs = []
+    for _ in range(iters):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        evs.append((s, e))
+    torch.cuda.synchronize()
+    t = sorted(s.elapsed_time(e) for s, e in evs)
+    return t[len(t) // 2], float(np.mean(t))
+
+
+def cpu_baseline(workloads):
+    """The oracle (untuned numpy + OpenBLAS float64) on a bounded sample of the
+    default workload: rows [0, 2080) of the 16640x5120x8192 blockwise forward
+    step (quantize those input rows and the full weight, then the GEMM)."""
+    from oracle import gemm as ogemm
+    from oracle import quant as oquant
+
+    Ms, N, K = 2080, 5120, 8192
+    inp = workloads.blockwise(M=16640, N=N, K=K)
+    x = inp["input"][:Ms]
+    w = inp["weight"]
+    t0 = time.perf_counter()
+    qx, sx = oquant.quantize_blockwise(x, 1, 128)
+    qw, sw = oquant.quantize_blockwise(w, 128, 128)
+    ogemm.scaled_mm(qx, qw, sx, "1x128", sw, "128x128")
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        threads = cores
+    return {"value": round(2.0 * Ms * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(min(cores, threads)),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"rows 0..{Ms} of the blockwise 1x128_128x128 forward step at 16640x5120x8192: "
+                      f"numpy oracle quantization of those input rows and the whole weight, float64 GEMM "
+                      f"({2.0 * Ms * N * K / 1e9:.0f} GFLOP), rounding to bf16"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the library is a single-GPU kernel library; see DESIGN.md for how it would shard)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import precision_matmul_amd as fp8mm
+    import workloads
+
+    fp8mm._lib.load()
+    torch.cuda.init()
+    W = build_workloads(torch, fp8mm, workloads)
+    if args.workload not in W:
+        raise SystemExit(f"unknown workload {args.workload}; choose from {sorted(W)}")
+
+    print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
+    wl = W[args.workload]()
+    torch.cuda.synchronize()
+
+    def step():
+        wl["quant"]()
+        return wl["gemm"]()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    gemm_events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        wl["quant"]()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        wl["gemm"]()
+        e.record()
+        gemm_events.append((s, e))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    gemm_ms = float(np.mean([s.elapsed_time(e) for s, e in gemm_events]))
+    value = wl["flops"] / (ms_step * 1e-3) / 1e12
+    achieved = wl["flops"] / (gemm_ms * 1e-3) / 1e12
+    print(f"[bench] step {ms_step:.3f} ms, gemm {gemm_ms:.3f} ms ({achieved:.1f} TFLOP/s)", file=sys.stderr,
+          flush=True)
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                traffic = json.load(f).get(args.workload)
+        except (OSError, ValueError):
+            traffic = None
+
+    result = {
+        "metric": "FP8 scaled-GEMM TFLOP/s at 1 MI355X + % of FP8 MFMA peak, per recipe",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic (seeded bf16 normals, shapes of the method's benchmarks)",
+        "config": {"workload": args.workload, "recipe": wl["recipe"], "shape_MNK": list(wl["shape"]),
+                   "step": "quantize both operands + scaled GEMM, bf16 out", "out_dtype": "bf16"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (" + wl["recipe"] + ")",
+                     "achieved": round(achieved, 2), "peak": FP8_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / FP8_DENSE_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_bytes": wl["gemm_bytes"], "gemm_ms": round(gemm_ms, 4)},
+    }
+
+    if not args.no_recipes:
+        per = {}
+        for name, make in W.items():
+            print(f"[bench] recipe workload {name}", file=sys.stderr, flush=True)
+            w2 = wl if name == args.workload else make()
+            w2["quant"]()
+            q_med, _ = time_kernel(torch, w2["quant"], 10)
+            g_med, _ = time_kernel(torch, w2["gemm"], 20)
+            per[name] = {"recipe": w2["recipe"], "gemm_ms": round(g_med, 4),
+                         "gemm_tflops": round(w2["flops"] / (g_med * 1e-3) / 1e12, 2),
+                         "gemm_frac_fp8_peak": round(w2["flops"] / (g_med * 1e-3) / 1e12 / FP8_DENSE_PEAK_TFLOPS, 4),
+                         "quant_ms": round(q_med, 4),
+                         "quant_GBps": round(w2["quant_bytes"] / (q_med * 1e-3) / 1e9, 1),
+                         "quant_frac_hbm_peak": round(w2["quant_bytes"] / (q_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if w2 is not wl:
+                del w2
+            torch.cuda.empty_cache()
+        result["per_recipe"] = per
+
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(workloads)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * fp8mm.h - C ABI of the MI355X (gfx950) FP8 scaled matrix-multiply library.
+ *
+ * The library computes   out = (A_fp8 * s_a) @ (B_fp8 * s_b)^T (+ bias)
+ * with FP8 E4M3 ("e4m3fn", max 448) operand codes and float32 scales, and the
+ * dynamic quantization pass that produces those codes and scales.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer except the ones marked "host" is a DEVICE pointer owned by
+ *     the caller.  The library never allocates, never frees and never
+ *     synchronizes: each call validates its arguments on the host, enqueues
+ *     kernels on `stream` and returns.  A NULL stream is the default stream.
+ *   - Matrices are row-major with an explicit leading dimension in elements.
+ *     bf16 is IEEE bfloat16 (uint16 storage); FP8 codes are uint8.
+ *   - Arguments are checked synchronously before anything is enqueued; a bad
+ *     argument returns FP8MM_EINVAL, a valid but unsupported combination
+ *     FP8MM_ENOTIMPL, and nothing is launched in either case.  A HIP launch
+ *     error returns FP8MM_ERUNTIME.  fp8mm_last_error() then gives a message.
+ *     (Error classes follow the review of pytorch PR #164141, "Add
+ *     _scaled_mm_v2 API": bad arguments are value errors, valid-but-missing
+ *     paths are not-implemented errors, device failures runtime errors.)
+ *   - There is no silent fallback: an unsupported path is an error, never a
+ *     dequantize-and-matmul substitute (pytorch/ao PR #4390, "Add _grouped_mm
+ *     dispatch handler to Float8Tensor", review).
+ *   - Alignment: base pointers of x, q, A and B are 16-byte aligned, their
+ *     leading dimensions are multiples of 16 bytes.
+ */
+#ifndef FP8MM_H
+#define FP8MM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8MM_OK = 0,
+  FP8MM_EINVAL = 1,   /* invalid argument (ValueError)                      */
+  FP8MM_ENOTIMPL = 2, /* valid but unsupported combination (NotImplemented) */
+  FP8MM_ERUNTIME = 3  /* HIP launch or device error (RuntimeError)           */
+} fp8mm_status;
+
+/* Scaling recipe of one operand (pytorch PR #164141, "Add _scaled_mm_v2
+ * API": the recipe of each operand is stated explicitly, never inferred).
+ * Scale arrays are dense float32, C order:
+ *   TENSORWISE      [1]
+ *   ROWWISE         A: [M]          B: [N]
+ *   BLOCK_1x128     A only: [K/128, M]        (k-block major)
+ *   BLOCK_128x128   B only: [N/128, K/128] for B_NK, [K/128, N/128] for B_KN
+ *                   (the quantizer's grid of B as stored)
+ *   BLOCK_128x1     B only: [K/128, N]  (128 along the contraction x 1 along
+ *                   N: the weight-gradient recipe of pytorch/ao PR #2784,
+ *                   "improve fp8 blockwise gemm perf", second table)     */
+typedef enum {
+  FP8MM_TENSORWISE = 0,
+  FP8MM_ROWWISE = 1,
+  FP8MM_BLOCK_1x128 = 2,
+  FP8MM_BLOCK_128x128 = 3,
+  FP8MM_BLOCK_128x1 = 4
+} fp8mm_recipe;
+
+/* Storage of the B operand.  B_NK: B[N, K], K contiguous (a weight as
+ * stored for input @ weight.t()).  B_KN: B[K, N], N contiguous (a weight as
+ * stored for grad_output @ weight). */
+typedef enum { FP8MM_B_NK = 0, FP8MM_B_KN = 1 } fp8mm_b_layout;
+
+typedef enum { FP8MM_OUT_BF16 = 0, FP8MM_OUT_FP32 = 1 } fp8mm_out_dtype;
+
+/* ---------------------------------------------------------------------------
+ * Dynamic quantization.  x: bf16 [rows, cols], leading dimension ld_x.
+ * q: uint8 E4M3 codes, leading dimension ld_q.  scale: float32 (layout below).
+ * For every scaling group G:  amax = max|x| over G;  s = fl32(amax / 448)
+ * (rowwise: fl32(fl32(amax / 448) + eps));  a scale of 0 becomes 1.0;
+ * code = e4m3(fl32(x / s)) rounded to nearest-even, saturated to +-448, sign
+ * kept.  The scale written is the dequantization multiplier (value = code*s).
+ * Sources: per-token scale from the row's max-abs value and division by it
+ * plus a small epsilon before the cast (DiffSynth-Engine PR #160, "per-token
+ * scaling for fp8 linear", "Highlights"); dequantization multipliers passed
+ * to the GEMM (ColossalAI PR #6419, "Fix: Handle LowLevelZeroPlugin with
+ * use_fp8=True", "Forward pass").
+ * Requirements: cols % 16 == 0, ld_x >= cols with ld_x % 8 == 0,
+ * ld_q % 16 == 0.  rows or cols of 0 is allowed (nothing but scales written).
+ * Results are bit-exact: independent of launch shape and run-to-run.
+ * ------------------------------------------------------------------------- */
+
+/* One scale for the whole tensor: scale[1].  ld_q >= cols.  Enqueues four
+ * small kernels (clear, amax, cast, finalize); `scale` doubles as the amax
+ * accumulator while they run. */
+fp8mm_status fp8_quantize_tensorwise(const void* x, int64_t rows, int64_t cols,
+                                     int64_t ld_x, uint8_t* q, int64_t ld_q,
+                                     float* scale, hipStream_t stream);
+
+/* One scale per row (per token): scale[rows].  eps >= 0 (1e-12 for the
+ * per-token recipe).  ld_q >= cols. */
+fp8mm_status fp8_quantize_rowwise(const void* x, int64_t rows, int64_t cols,
+                                  int64_t ld_x, float eps, uint8_t* q,
+                                  int64_t ld_q, float* scale,
+                                  hipStream_t stream);
+
+/* Block groups of block_rows x block_cols, one of
+ *   (1, 128)   scale[cols/128, rows]            (activation, k-block major)
+ *   (128, 128) scale[rows/128, cols/128]        (weight)
+ *   (128, 1)   scale[rows/128, cols]            (weight-gradient operands)
+ * rows % block_rows == 0 and cols % block_cols == 0.
+ * transpose_out = 1 (only with (128, 1)) writes the codes transposed,
+ * q[cols, rows] with ld_q >= rows (rows % 16 == 0), so that the token
+ * dimension becomes the contiguous contraction dimension of the weight-
+ * gradient GEMM; otherwise q[rows, cols] with ld_q >= cols. */
+fp8mm_status fp8_quantize_blockwise(const void* x, int64_t rows, int64_t cols,
+                                    int64_t ld_x, int block_rows,
+                                    int block_cols, int transpose_out,
+                                    uint8_t* q, int64_t ld_q, float* scale,
+                                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Scaled GEMM:  out[M, N] = sum_k (A[i,k] s_a(i,k)) (B(j,k) s_b(j,k)) (+bias[j])
+ * with float32 accumulation on the matrix cores and one final rounding to
+ * out_dtype (bf16 round-to-nearest-even or fp32).  The formulation is the
+ * fused scaled-mm call whose dequantize-then-matmul equivalent is spelled out
+ * in ColossalAI PR #6419 ("Forward pass", "Backward pass").
+ *   A: uint8 [M, K], leading dimension lda (K contiguous).
+ *   B: uint8 [N, K] (B_NK, ldb >= K) or [K, N] (B_KN, ldb >= N).
+ *   scale_a / scale_b: float32 in the layouts of fp8mm_recipe.
+ *   bias: NULL or bf16 [N], added in fp32 before the rounding.
+ *   out: bf16 or fp32 [M, N], leading dimension ldo >= N.
+ * Accepted (recipe_a, recipe_b) pairs, anything else -> FP8MM_ENOTIMPL:
+ *   (TENSORWISE, TENSORWISE)  (ROWWISE, ROWWISE)
+ *   (BLOCK_1x128, BLOCK_128x128)  (BLOCK_1x128, BLOCK_128x1)
+ * K % 16 == 0; blockwise recipes need K % 128 == 0 and, for BLOCK_128x128,
+ * N % 128 == 0.  M, N or K of 0 is allowed. */
+fp8mm_status fp8_scaled_mm(const uint8_t* A, int64_t M, int64_t K, int64_t lda,
+                           const uint8_t* B, int64_t N, int64_t ldb,
+                           fp8mm_b_layout b_layout, const float* scale_a,
+                           fp8mm_recipe recipe_a, const float* scale_b,
+                           fp8mm_recipe recipe_b, const void* bias,
+                           fp8mm_out_dtype out_dtype, void* out, int64_t ldo,
+                           hipStream_t stream);
+
+/* Grouped (MoE) scaled GEMM, rowwise x rowwise only, in the canonical form
+ * grouped_mm(act, weight.transpose(-2, -1), offs) of pytorch/ao PR #4390
+ * ("Add _grouped_mm dispatch handler to Float8Tensor", "Design" and review):
+ *   A: uint8 [M_total, K] (lda = K), scale_a float32 [M_total] (per token).
+ *   B_EnK: uint8 [E, N, K] expert weights (K contiguous), scale_b [E, N].
+ *   offsets: DEVICE int32 [E], cumulative END row offsets: expert e owns rows
+ *     [offsets[e-1], offsets[e]) (offsets[-1] = 0); required (NULL -> EINVAL).
+ *   bias: NULL or bf16 [E, N] (per expert).
+ *   out: [M_total, N], leading dimension ldo >= N.  Rows at or past
+ *     offsets[E-1] are not written.
+ * Offsets are read on the device only; they are not validated on the host
+ * (that would need a synchronization).  The kernels clamp them to
+ * [0, M_total] and treat a decreasing pair as an empty group.
+ * K % 16 == 0. */
+fp8mm_status fp8_scaled_grouped_mm(const uint8_t* A, int64_t M_total,
+                                   int64_t K, const uint8_t* B_EnK, int64_t E,
+                                   int64_t N, const int32_t* offsets,
+                                   const float* scale_a, const float* scale_b,
+                                   const void* bias, fp8mm_out_dtype out_dtype,
+                                   void* out, int64_t ldo, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * The three call forms of an FP8 linear layer (ColossalAI PR #6419, "Forward
+ * pass" and "Backward pass"; pytorch/ao PR #2784 names the blockwise GEMMs
+ * each one uses).  All operands are pre-quantized, dense (leading dimension =
+ * row length), and the calls are thin wrappers over fp8_scaled_mm.
+ * ------------------------------------------------------------------------- */
+
+/* out[M, N] = input @ weight.t():  input codes [M, K] (recipe x_recipe),
+ * weight codes [N, K] (recipe w_recipe, read as B_NK), bias NULL or [N]. */
+fp8mm_status fp8_linear_forward(const uint8_t* x_q, int64_t M, int64_t K,
+                                const float* x_scale, fp8mm_recipe x_recipe,
+                                const uint8_t* w_q, int64_t N,
+                                const float* w_scale, fp8mm_recipe w_recipe,
+                                const void* bias, fp8mm_out_dtype out_dtype,
+                                void* out, hipStream_t stream);
+
+/* grad_input[M, K_in] = grad_output @ weight:  grad_output codes [M, N_out]
+ * (recipe g_recipe, contraction over N_out), weight codes as stored
+ * [N_out, K_in] (recipe w_recipe, read as B_KN). */
+fp8mm_status fp8_linear_grad_input(const uint8_t* g_q, int64_t M,
+                                   int64_t N_out, const float* g_scale,
+                                   fp8mm_recipe g_recipe, const uint8_t* w_q,
+                                   int64_t K_in, const float* w_scale,
+                                   fp8mm_recipe w_recipe,
+                                   fp8mm_out_dtype out_dtype, void* grad_in,
+                                   hipStream_t stream);
+
+/* grad_weight[N_out, K_in] = grad_output.t() @ input, contracting over T
+ * tokens.  Both operands come from fp8_quantize_blockwise with block (128, 1)
+ * and transpose_out = 1:  gt_q = codes of grad_output^T [N_out, T] with
+ * gt_scale [T/128, N_out];  xt_q = codes of input^T [K_in, T] with xt_scale
+ * [T/128, K_in].  Recipes: (BLOCK_1x128, BLOCK_128x1), B read as B_NK. */
+fp8mm_status fp8_linear_grad_weight(const uint8_t* gt_q, int64_t N_out,
+                                    int64_t T, const float* gt_scale,
+                                    const uint8_t* xt_q, int64_t K_in,
+                                    const float* xt_scale,
+                                    fp8mm_out_dtype out_dtype, void* grad_w,
+                                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Host-only queries (no device access).
+ * ------------------------------------------------------------------------- */
+
+/* 1 if fp8_scaled_mm accepts the recipe pair with this B layout, else 0. */
+int fp8mm_recipe_pair_supported(fp8mm_recipe recipe_a, fp8mm_recipe recipe_b,
+                                fp8mm_b_layout b_layout);
+
+/* Message describing the last non-OK status returned on the calling thread
+ * (empty string if none).  Owned by the library; valid until the next call on
+ * the same thread. */
+const char* fp8mm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8MM_H */

@@ -1,0 +1,270 @@
+"""FP8 scaled matrix multiply for AMD MI355X (gfx950).
+
+Python binding over the C ABI of ``libfp8mm.so`` (include/fp8mm.h).  The
+functions carry the C names; they only check and marshal arguments, allocate
+outputs with torch and pass device pointers plus the current HIP stream.
+Every step of the computation runs in the library's HIP kernels.
+
+Recipes are named "tensorwise", "rowwise", "1x128", "128x128" and "128x1";
+scales are always returned as 2-D float32 tensors:
+  tensorwise [1, 1]     rowwise [rows, 1]     1x128 [cols/128, rows]
+  128x128 [rows/128, cols/128]                128x1 [rows/128, cols]
+Errors map to ValueError (bad arguments), NotImplementedError (valid but not
+supported) and RuntimeError (HIP failures).
+"""
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "fp8_quantize_tensorwise", "fp8_quantize_rowwise", "fp8_quantize_blockwise",
+    "fp8_scaled_mm", "fp8_scaled_grouped_mm", "fp8_linear_forward",
+    "fp8_linear_grad_input", "fp8_linear_grad_weight", "recipe_pair_supported",
+]
+
+ROWWISE_EPS = 1e-12
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _ld(t, name):
+    """Leading dimension of a row-major 2-D tensor (unit column stride)."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D row-major tensor")
+    if t.shape[0] > 1 and t.shape[1] > 0:
+        return t.stride(0)
+    return _ld16(t.shape[1])     # one row or no columns: any padded width will do
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _recipe(r):
+    if isinstance(r, str):
+        if r not in _lib.RECIPES:
+            raise ValueError(f"unknown recipe {r!r}")
+        return _lib.RECIPES[r]
+    return int(r)
+
+
+def _out_code(dtype):
+    if dtype == torch.bfloat16:
+        return _lib.OUT_BF16
+    if dtype == torch.float32:
+        return _lib.OUT_FP32
+    raise ValueError(f"out_dtype must be torch.bfloat16 or torch.float32, got {dtype}")
+
+
+def _ld16(n):
+    return max(16, (n + 15) // 16 * 16)
+
+
+def _check_scale(scale, recipe, operand, M, N, K):
+    """The C ABI takes bare pointers, so the element count of each scale
+    array is checked here against its recipe (see fp8mm_recipe)."""
+    r = _recipe(recipe)
+    rows = M if operand == "a" else N
+    want = {0: 1, 1: rows}
+    if operand == "a":
+        want[2] = (K // 128) * M
+    else:
+        want[3] = (N // 128) * (K // 128)
+        want[4] = (K // 128) * N
+    if r in want and scale.numel() != want[r]:
+        raise ValueError(f"scale_{operand} has {scale.numel()} elements, recipe needs {want[r]}")
+
+
+def fp8_quantize_tensorwise(x):
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((1, 1), dtype=torch.float32, device=x.device)
+    st = _lib.load().fp8_quantize_tensorwise(x.data_ptr(), rows, cols, _ld(x, "x"), q.data_ptr(),
+                                             _ld(q, "q"), s.data_ptr(), _stream(x))
+    _lib.check(st, "fp8_quantize_tensorwise")
+    return q, s
+
+
+def fp8_quantize_rowwise(x, eps=ROWWISE_EPS):
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((rows, 1), dtype=torch.float32, device=x.device)
+    st = _lib.load().fp8_quantize_rowwise(x.data_ptr(), rows, cols, _ld(x, "x"), float(eps), q.data_ptr(),
+                                          _ld(q, "q"), s.data_ptr(), _stream(x))
+    _lib.check(st, "fp8_quantize_rowwise")
+    return q, s
+
+
+def fp8_quantize_blockwise(x, block=(1, 128), transpose_out=False):
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    br, bc = int(block[0]), int(block[1])
+    if br <= 0 or bc <= 0 or rows % br or cols % bc:
+        raise ValueError(f"shape {tuple(x.shape)} is not a multiple of block {(br, bc)}")
+    qshape = (cols, rows) if transpose_out else (rows, cols)
+    q = torch.empty(qshape, dtype=torch.uint8, device=x.device)
+    if (br, bc) == (1, 128):
+        sshape = (cols // 128, rows)
+    elif (br, bc) == (128, 1):
+        sshape = (rows // 128, cols)
+    else:
+        sshape = (rows // br, cols // bc)
+    s = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    st = _lib.load().fp8_quantize_blockwise(x.data_ptr(), rows, cols, _ld(x, "x"), br, bc, int(bool(transpose_out)),
+                                            q.data_ptr(), _ld(q, "q"), s.data_ptr(), _stream(x))
+    _lib.check(st, "fp8_quantize_blockwise")
+    return q, s
+
+
+def fp8_scaled_mm(A, B, scale_a, recipe_a, scale_b, recipe_b, b_layout="NK", bias=None,
+                  out_dtype=torch.bfloat16, out=None):
+    """out = (A * s_a) @ (B * s_b)^T (+ bias).  A uint8 [M, K]; B uint8
+    [N, K] (b_layout "NK") or [K, N] ("KN")."""
+    _need(A, torch.uint8, "A")
+    _need(B, torch.uint8, "B")
+    _need(scale_a, torch.float32, "scale_a")
+    _need(scale_b, torch.float32, "scale_b")
+    if b_layout not in _lib.B_LAYOUTS:
+        raise ValueError(f"b_layout must be 'NK' or 'KN', got {b_layout!r}")
+    if not (scale_a.is_contiguous() and scale_b.is_contiguous()):
+        raise ValueError("scales must be contiguous")
+    M, K = A.shape
+    N = B.shape[0] if b_layout == "NK" else B.shape[1]
+    kb = B.shape[1] if b_layout == "NK" else B.shape[0]
+    if kb != K:
+        raise ValueError(f"contraction mismatch: A has K={K}, B has {kb}")
+    _check_scale(scale_a, recipe_a, "a", M, N, K)
+    _check_scale(scale_b, recipe_b, "b", M, N, K)
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias")
+        if bias.numel() != N or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous bf16 tensor of N elements")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong dtype or shape")
+    st = _lib.load().fp8_scaled_mm(A.data_ptr(), M, K, _ld(A, "A"), B.data_ptr(), N, _ld(B, "B"),
+                                   _lib.B_LAYOUTS[b_layout], scale_a.data_ptr(), _recipe(recipe_a),
+                                   scale_b.data_ptr(), _recipe(recipe_b), _ptr(bias), _out_code(out_dtype),
+                                   out.data_ptr(), _ld(out, "out"), _stream(A))
+    _lib.check(st, "fp8_scaled_mm")
+    return out
+
+
+def fp8_scaled_grouped_mm(A, B_EnK, offsets, scale_a, scale_b, bias=None, out_dtype=torch.bfloat16, out=None):
+    """Grouped (MoE) GEMM in the form grouped_mm(act, weight.transpose(-2, -1),
+    offs): A uint8 [M_total, K], B_EnK uint8 [E, N, K], offsets int32 [E]
+    (cumulative end rows), rowwise scales scale_a [M_total] and scale_b [E, N].
+    Rows at or past offsets[-1] are left as they are in `out` (zeros when the
+    output is allocated here)."""
+    if offsets is None:
+        raise ValueError("offsets are required for the grouped GEMM")
+    _need(A, torch.uint8, "A")
+    _need(B_EnK, torch.uint8, "B_EnK")
+    _need(offsets, torch.int32, "offsets")
+    _need(scale_a, torch.float32, "scale_a")
+    _need(scale_b, torch.float32, "scale_b")
+    if B_EnK.dim() != 3 or not B_EnK.is_contiguous() or not A.is_contiguous():
+        raise ValueError("A must be contiguous [M_total, K] and B_EnK contiguous [E, N, K]")
+    M, K = A.shape
+    E, N, K2 = B_EnK.shape
+    if K2 != K:
+        raise ValueError(f"contraction mismatch: A has K={K}, B_EnK has {K2}")
+    if offsets.numel() != E or not offsets.is_contiguous():
+        raise ValueError("offsets must be a contiguous int32 tensor of E elements")
+    if scale_a.numel() != M or scale_b.numel() != E * N:
+        raise ValueError("rowwise scales must have M_total and E*N elements")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias")
+        if bias.numel() != E * N or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous bf16 [E, N] tensor")
+    if out is None:
+        out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
+    st = _lib.load().fp8_scaled_grouped_mm(A.data_ptr(), M, K, B_EnK.data_ptr(), E, N, offsets.data_ptr(),
+                                           scale_a.data_ptr(), scale_b.data_ptr(), _ptr(bias),
+                                           _out_code(out_dtype), out.data_ptr(), _ld(out, "out"), _stream(A))
+    _lib.check(st, "fp8_scaled_grouped_mm")
+    return out
+
+
+def fp8_linear_forward(x_q, x_scale, x_recipe, w_q, w_scale, w_recipe, bias=None, out_dtype=torch.bfloat16):
+    """out = input @ weight.t(): x_q [M, K], w_q [N, K]."""
+    for t, n in ((x_q, "x_q"), (w_q, "w_q")):
+        _need(t, torch.uint8, n)
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] != K or not (x_q.is_contiguous() and w_q.is_contiguous()):
+        raise ValueError("x_q [M, K] and w_q [N, K] must be contiguous with equal K")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias")
+        if bias.numel() != N or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous bf16 tensor of N elements")
+    for t, n in ((x_scale, "x_scale"), (w_scale, "w_scale")):
+        _need(t, torch.float32, n)
+    _check_scale(x_scale, x_recipe, "a", M, N, K)
+    _check_scale(w_scale, w_recipe, "b", M, N, K)
+    out = torch.empty((M, N), dtype=out_dtype, device=x_q.device)
+    st = _lib.load().fp8_linear_forward(x_q.data_ptr(), M, K, x_scale.data_ptr(), _recipe(x_recipe), w_q.data_ptr(),
+                                        N, w_scale.data_ptr(), _recipe(w_recipe), _ptr(bias),
+                                        _out_code(out_dtype), out.data_ptr(), _stream(x_q))
+    _lib.check(st, "fp8_linear_forward")
+    return out
+
+
+def fp8_linear_grad_input(g_q, g_scale, g_recipe, w_q, w_scale, w_recipe, out_dtype=torch.bfloat16):
+    """grad_input = grad_output @ weight: g_q [M, N_out], w_q [N_out, K_in]."""
+    for t, n in ((g_q, "g_q"), (w_q, "w_q")):
+        _need(t, torch.uint8, n)
+    M, N_out = g_q.shape
+    if w_q.shape[0] != N_out or not (g_q.is_contiguous() and w_q.is_contiguous()):
+        raise ValueError("g_q [M, N_out] and w_q [N_out, K_in] must be contiguous")
+    K_in = w_q.shape[1]
+    for t, n in ((g_scale, "g_scale"), (w_scale, "w_scale")):
+        _need(t, torch.float32, n)
+    _check_scale(g_scale, g_recipe, "a", M, K_in, N_out)
+    _check_scale(w_scale, w_recipe, "b", M, K_in, N_out)
+    out = torch.empty((M, K_in), dtype=out_dtype, device=g_q.device)
+    st = _lib.load().fp8_linear_grad_input(g_q.data_ptr(), M, N_out, g_scale.data_ptr(), _recipe(g_recipe),
+                                           w_q.data_ptr(), K_in, w_scale.data_ptr(), _recipe(w_recipe),
+                                           _out_code(out_dtype), out.data_ptr(), _stream(g_q))
+    _lib.check(st, "fp8_linear_grad_input")
+    return out
+
+
+def fp8_linear_grad_weight(gt_q, gt_scale, xt_q, xt_scale, out_dtype=torch.bfloat16):
+    """grad_weight = grad_output.t() @ input from (128, 1)-quantized,
+    transposed operands: gt_q [N_out, T], xt_q [K_in, T]."""
+    for t, n in ((gt_q, "gt_q"), (xt_q, "xt_q")):
+        _need(t, torch.uint8, n)
+    N_out, T = gt_q.shape
+    if xt_q.shape[1] != T or not (gt_q.is_contiguous() and xt_q.is_contiguous()):
+        raise ValueError("gt_q [N_out, T] and xt_q [K_in, T] must be contiguous with equal T")
+    K_in = xt_q.shape[0]
+    for t, n in ((gt_scale, "gt_scale"), (xt_scale, "xt_scale")):
+        _need(t, torch.float32, n)
+    _check_scale(gt_scale, "1x128", "a", N_out, K_in, T)
+    _check_scale(xt_scale, "128x1", "b", N_out, K_in, T)
+    out = torch.empty((N_out, K_in), dtype=out_dtype, device=gt_q.device)
+    st = _lib.load().fp8_linear_grad_weight(gt_q.data_ptr(), N_out, T, gt_scale.data_ptr(), xt_q.data_ptr(), K_in,
+                                            xt_scale.data_ptr(), _out_code(out_dtype), out.data_ptr(), _stream(gt_q))
+    _lib.check(st, "fp8_linear_grad_weight")
+    return out
+
+
+def recipe_pair_supported(recipe_a, recipe_b, b_layout="NK"):
+    return bool(_lib.load().fp8mm_recipe_pair_supported(_recipe(recipe_a), _recipe(recipe_b),
+                                                        _lib.B_LAYOUTS[b_layout]))

@@ -1,0 +1,256 @@
+// C ABI of the FP8 scaled-GEMM library: host-side argument validation, the
+// recipe-pair table and kernel dispatch.  Nothing here allocates, frees or
+// synchronizes; every accepted call only enqueues kernels on the caller's
+// stream.
+//
+// The explicit per-operand recipe checked against a table of accepted pairs,
+// and the split of failures into value errors, not-implemented errors and
+// runtime errors, follow the design discussed in pytorch PR #164141 ("Add
+// _scaled_mm_v2 API").  Unsupported combinations fail loudly instead of
+// falling back to a dequantized matmul (pytorch/ao PR #4390, "Add
+// _grouped_mm dispatch handler to Float8Tensor", review).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/fp8mm.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fp8mm_status fail(fp8mm_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+fp8mm_status ok() {
+  g_last_error[0] = '\0';
+  return FP8MM_OK;
+}
+
+fp8mm_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FP8MM_ERUNTIME, "%s: HIP error %d (%s)", what, int(e), hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Offsets are formed in 32-bit buffer descriptors: keep one tile's span of
+// an operand below 2^31 bytes.
+constexpr int64_t kMaxLd = int64_t(1) << 22;
+
+struct PairRule {
+  fp8mm_recipe a;
+  fp8mm_recipe b;
+  fp8mm::Epi epi;
+  const char* name;
+};
+
+// The accepted (recipe_a, recipe_b) pairs.  Each operand names its own
+// recipe; nothing is inferred from scale shapes.
+constexpr PairRule kPairs[] = {
+    {FP8MM_TENSORWISE, FP8MM_TENSORWISE, fp8mm::Epi::Tensor, "tensorwise_tensorwise"},
+    {FP8MM_ROWWISE, FP8MM_ROWWISE, fp8mm::Epi::Row, "rowwise_rowwise"},
+    {FP8MM_BLOCK_1x128, FP8MM_BLOCK_128x128, fp8mm::Epi::Block128x128, "blockwise_1x128_128x128"},
+    {FP8MM_BLOCK_1x128, FP8MM_BLOCK_128x1, fp8mm::Epi::Block128x1, "blockwise_1x128_128x1"},
+};
+
+const PairRule* find_pair(fp8mm_recipe a, fp8mm_recipe b) {
+  for (const PairRule& r : kPairs)
+    if (r.a == a && r.b == b) return &r;
+  return nullptr;
+}
+
+bool valid_recipe(int r) { return r >= FP8MM_TENSORWISE && r <= FP8MM_BLOCK_128x1; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8mm_last_error(void) { return g_last_error; }
+
+int fp8mm_recipe_pair_supported(fp8mm_recipe recipe_a, fp8mm_recipe recipe_b, fp8mm_b_layout b_layout) {
+  if (b_layout != FP8MM_B_NK && b_layout != FP8MM_B_KN) return 0;
+  return find_pair(recipe_a, recipe_b) != nullptr ? 1 : 0;
+}
+
+// ----------------------------------------------------------------- quantize
+
+static fp8mm_status check_quant_common(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                       const uint8_t* q, const float* scale) {
+  if (rows < 0 || cols < 0) return fail(FP8MM_EINVAL, "negative shape [%lld, %lld]", (long long)rows, (long long)cols);
+  // x and q may be NULL for an empty matrix; whether scale may be NULL
+  // depends on whether the recipe writes any scale (checked by the caller).
+  if (rows > 0 && cols > 0 && (!x || !q))
+    return fail(FP8MM_EINVAL, "null pointer (x=%p q=%p)", x, (const void*)q);
+  (void)scale;
+  if (cols % 16 != 0) return fail(FP8MM_EINVAL, "cols (%lld) must be a multiple of 16", (long long)cols);
+  if (ld_x < cols || ld_x % 8 != 0 || ld_x > kMaxLd)
+    return fail(FP8MM_EINVAL, "ld_x (%lld) must be >= cols (%lld), a multiple of 8 and <= 2^22", (long long)ld_x, (long long)cols);
+  if (!aligned16(x) || !aligned16(q)) return fail(FP8MM_EINVAL, "x and q must be 16-byte aligned");
+  if (rows > (int64_t(1) << 31) - 1 || cols > (int64_t(1) << 31) - 1) return fail(FP8MM_EINVAL, "rows and cols must be < 2^31");
+  return FP8MM_OK;
+}
+
+fp8mm_status fp8_quantize_tensorwise(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                                     int64_t ld_q, float* scale, hipStream_t stream) {
+  fp8mm_status st = check_quant_common(x, rows, cols, ld_x, q, scale);
+  if (st != FP8MM_OK) return st;
+  if (!scale) return fail(FP8MM_EINVAL, "scale must not be NULL");
+  if (ld_q < cols || ld_q % 16 != 0) return fail(FP8MM_EINVAL, "ld_q (%lld) must be >= cols and a multiple of 16", (long long)ld_q);
+  return from_hip(fp8mm::launch_quant_tensorwise(static_cast<const uint16_t*>(x), rows, cols, ld_x, q, ld_q, scale, stream),
+                  "fp8_quantize_tensorwise");
+}
+
+fp8mm_status fp8_quantize_rowwise(const void* x, int64_t rows, int64_t cols, int64_t ld_x, float eps, uint8_t* q,
+                                  int64_t ld_q, float* scale, hipStream_t stream) {
+  fp8mm_status st = check_quant_common(x, rows, cols, ld_x, q, scale);
+  if (st != FP8MM_OK) return st;
+  if (!scale && rows > 0) return fail(FP8MM_EINVAL, "scale must not be NULL");
+  if (ld_q < cols || ld_q % 16 != 0) return fail(FP8MM_EINVAL, "ld_q (%lld) must be >= cols and a multiple of 16", (long long)ld_q);
+  if (!(eps >= 0.0f) || eps != eps || eps > 1e30f) return fail(FP8MM_EINVAL, "eps must be a finite value >= 0");
+  return from_hip(fp8mm::launch_quant_rowwise(static_cast<const uint16_t*>(x), rows, cols, ld_x, eps, q, ld_q, scale, stream),
+                  "fp8_quantize_rowwise");
+}
+
+fp8mm_status fp8_quantize_blockwise(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int block_rows,
+                                    int block_cols, int transpose_out, uint8_t* q, int64_t ld_q, float* scale,
+                                    hipStream_t stream) {
+  fp8mm_status st = check_quant_common(x, rows, cols, ld_x, q, scale);
+  if (st != FP8MM_OK) return st;
+  if (!scale && rows > 0 && cols > 0) return fail(FP8MM_EINVAL, "scale must not be NULL");
+  const bool b1x128 = block_rows == 1 && block_cols == 128;
+  const bool b128x128 = block_rows == 128 && block_cols == 128;
+  const bool b128x1 = block_rows == 128 && block_cols == 1;
+  if (!b1x128 && !b128x128 && !b128x1)
+    return fail(FP8MM_ENOTIMPL, "block shape (%d, %d) is not one of (1,128), (128,128), (128,1)", block_rows, block_cols);
+  if (transpose_out != 0 && transpose_out != 1) return fail(FP8MM_EINVAL, "transpose_out must be 0 or 1");
+  if (transpose_out && !b128x1) return fail(FP8MM_ENOTIMPL, "transpose_out is only implemented for block (128, 1)");
+  if (rows % block_rows != 0 || cols % block_cols != 0)
+    return fail(FP8MM_EINVAL, "shape [%lld, %lld] is not a multiple of block (%d, %d)", (long long)rows, (long long)cols,
+                block_rows, block_cols);
+  const int64_t q_width = transpose_out ? rows : cols;
+  if (ld_q < q_width || ld_q % 16 != 0 || ld_q > kMaxLd)
+    return fail(FP8MM_EINVAL, "ld_q (%lld) must be >= %lld and a multiple of 16", (long long)ld_q, (long long)q_width);
+  return from_hip(fp8mm::launch_quant_blockwise(static_cast<const uint16_t*>(x), rows, cols, ld_x, block_rows, block_cols,
+                                                transpose_out, q, ld_q, scale, stream),
+                  "fp8_quantize_blockwise");
+}
+
+// --------------------------------------------------------------------- GEMM
+
+fp8mm_status fp8_scaled_mm(const uint8_t* A, int64_t M, int64_t K, int64_t lda, const uint8_t* B, int64_t N,
+                           int64_t ldb, fp8mm_b_layout b_layout, const float* scale_a, fp8mm_recipe recipe_a,
+                           const float* scale_b, fp8mm_recipe recipe_b, const void* bias, fp8mm_out_dtype out_dtype,
+                           void* out, int64_t ldo, hipStream_t stream) {
+  if (!valid_recipe(recipe_a) || !valid_recipe(recipe_b)) return fail(FP8MM_EINVAL, "unknown recipe value");
+  if (b_layout != FP8MM_B_NK && b_layout != FP8MM_B_KN) return fail(FP8MM_EINVAL, "unknown B layout");
+  if (out_dtype != FP8MM_OUT_BF16 && out_dtype != FP8MM_OUT_FP32) return fail(FP8MM_EINVAL, "unknown out_dtype");
+  if (M < 0 || N < 0 || K < 0) return fail(FP8MM_EINVAL, "negative shape M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
+  if (M > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1) return fail(FP8MM_EINVAL, "M and N must be < 2^31");
+  const PairRule* rule = find_pair(recipe_a, recipe_b);
+  if (!rule) return fail(FP8MM_ENOTIMPL, "recipe pair (%d, %d) is not implemented", int(recipe_a), int(recipe_b));
+  const bool blockwise = rule->epi == fp8mm::Epi::Block128x128 || rule->epi == fp8mm::Epi::Block128x1;
+  if (K % 16 != 0) return fail(FP8MM_EINVAL, "K (%lld) must be a multiple of 16", (long long)K);
+  if (blockwise && K % 128 != 0) return fail(FP8MM_EINVAL, "%s needs K %% 128 == 0 (K=%lld)", rule->name, (long long)K);
+  if (rule->epi == fp8mm::Epi::Block128x128 && N % 128 != 0)
+    return fail(FP8MM_EINVAL, "%s needs N %% 128 == 0 (N=%lld)", rule->name, (long long)N);
+  if (lda < K || lda % 16 != 0 || lda > kMaxLd) return fail(FP8MM_EINVAL, "lda (%lld) must be >= K, a multiple of 16 and <= 2^22", (long long)lda);
+  const int64_t b_width = b_layout == FP8MM_B_NK ? K : N;
+  if (ldb < b_width || ldb % 16 != 0 || ldb > kMaxLd)
+    return fail(FP8MM_EINVAL, "ldb (%lld) must be >= %lld, a multiple of 16 and <= 2^22", (long long)ldb, (long long)b_width);
+  if (b_layout == FP8MM_B_KN && K * ldb > (int64_t(1) << 31))
+    return fail(FP8MM_EINVAL, "B stored [K, N] must span fewer than 2^31 bytes");
+  if (ldo < N) return fail(FP8MM_EINVAL, "ldo (%lld) must be >= N (%lld)", (long long)ldo, (long long)N);
+  if (M == 0 || N == 0) return ok();
+  if (!scale_a || !scale_b || !out) return fail(FP8MM_EINVAL, "null pointer argument (scales and out are required)");
+  if (K > 0 && (!A || !B)) return fail(FP8MM_EINVAL, "null pointer argument (A and B are required when K > 0)");
+  if (!aligned16(A) || !aligned16(B)) return fail(FP8MM_EINVAL, "A and B must be 16-byte aligned");
+  fp8mm::GemmProblem p{};
+  p.A = A;
+  p.B = B;
+  p.sa = scale_a;
+  p.sb = scale_b;
+  p.bias = static_cast<const uint16_t*>(bias);
+  p.out = out;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldo = ldo;
+  p.epi = rule->epi;
+  p.b_kn = b_layout == FP8MM_B_KN;
+  p.out_bf16 = out_dtype == FP8MM_OUT_BF16;
+  p.offsets = nullptr;
+  p.E = 0;
+  return from_hip(fp8mm::launch_gemm(p, stream), "fp8_scaled_mm");
+}
+
+fp8mm_status fp8_scaled_grouped_mm(const uint8_t* A, int64_t M_total, int64_t K, const uint8_t* B_EnK, int64_t E,
+                                   int64_t N, const int32_t* offsets, const float* scale_a, const float* scale_b,
+                                   const void* bias, fp8mm_out_dtype out_dtype, void* out, int64_t ldo,
+                                   hipStream_t stream) {
+  if (!offsets) return fail(FP8MM_EINVAL, "offsets are required for the grouped GEMM");
+  if (out_dtype != FP8MM_OUT_BF16 && out_dtype != FP8MM_OUT_FP32) return fail(FP8MM_EINVAL, "unknown out_dtype");
+  if (M_total < 0 || K < 0 || N < 0 || E < 0) return fail(FP8MM_EINVAL, "negative shape");
+  if (M_total > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1 || E > (int64_t(1) << 20))
+    return fail(FP8MM_EINVAL, "M_total and N must be < 2^31 and E <= 2^20");
+  if (K % 16 != 0 || K > kMaxLd) return fail(FP8MM_EINVAL, "K (%lld) must be a multiple of 16 and <= 2^22", (long long)K);
+  if (ldo < N) return fail(FP8MM_EINVAL, "ldo (%lld) must be >= N (%lld)", (long long)ldo, (long long)N);
+  if (M_total == 0 || N == 0 || E == 0) return ok();
+  if (!scale_a || !scale_b || !out) return fail(FP8MM_EINVAL, "null pointer argument (scales and out are required)");
+  if (K > 0 && (!A || !B_EnK)) return fail(FP8MM_EINVAL, "null pointer argument (A and B_EnK are required when K > 0)");
+  if (!aligned16(A) || !aligned16(B_EnK)) return fail(FP8MM_EINVAL, "A and B_EnK must be 16-byte aligned");
+  fp8mm::GemmProblem p{};
+  p.A = A;
+  p.B = B_EnK;
+  p.sa = scale_a;
+  p.sb = scale_b;
+  p.bias = static_cast<const uint16_t*>(bias);
+  p.out = out;
+  p.M = M_total;
+  p.N = N;
+  p.K = K;
+  p.lda = K;
+  p.ldb = K;
+  p.ldo = ldo;
+  p.epi = fp8mm::Epi::Row;
+  p.b_kn = false;
+  p.out_bf16 = out_dtype == FP8MM_OUT_BF16;
+  p.offsets = offsets;
+  p.E = E;
+  return from_hip(fp8mm::launch_gemm(p, stream), "fp8_scaled_grouped_mm");
+}
+
+// ------------------------------------------------------------- call forms
+
+fp8mm_status fp8_linear_forward(const uint8_t* x_q, int64_t M, int64_t K, const float* x_scale,
+                                fp8mm_recipe x_recipe, const uint8_t* w_q, int64_t N, const float* w_scale,
+                                fp8mm_recipe w_recipe, const void* bias, fp8mm_out_dtype out_dtype, void* out,
+                                hipStream_t stream) {
+  return fp8_scaled_mm(x_q, M, K, K, w_q, N, K, FP8MM_B_NK, x_scale, x_recipe, w_scale, w_recipe, bias, out_dtype,
+                       out, N, stream);
+}
+
+fp8mm_status fp8_linear_grad_input(const uint8_t* g_q, int64_t M, int64_t N_out, const float* g_scale,
+                                   fp8mm_recipe g_recipe, const uint8_t* w_q, int64_t K_in, const float* w_scale,
+                                   fp8mm_recipe w_recipe, fp8mm_out_dtype out_dtype, void* grad_in,
+                                   hipStream_t stream) {
+  // contraction over N_out: A = grad_output [M, N_out], B = weight [N_out, K_in] read as [K, N]
+  return fp8_scaled_mm(g_q, M, N_out, N_out, w_q, K_in, K_in, FP8MM_B_KN, g_scale, g_recipe, w_scale, w_recipe,
+                       nullptr, out_dtype, grad_in, K_in, stream);
+}
+
+fp8mm_status fp8_linear_grad_weight(const uint8_t* gt_q, int64_t N_out, int64_t T, const float* gt_scale,
+                                    const uint8_t* xt_q, int64_t K_in, const float* xt_scale,
+                                    fp8mm_out_dtype out_dtype, void* grad_w, hipStream_t stream) {
+  return fp8_scaled_mm(gt_q, N_out, T, T, xt_q, K_in, T, FP8MM_B_NK, gt_scale, FP8MM_BLOCK_1x128, xt_scale,
+                       FP8MM_BLOCK_128x1, nullptr, out_dtype, grad_w, K_in, stream);
+}
+
+}  // extern "C"

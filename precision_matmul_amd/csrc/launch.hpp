@@ -1,0 +1,44 @@
+// Kernel launchers shared between the C ABI layer and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8mm {
+
+hipError_t launch_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   uint8_t* q, int64_t ld_q, float* scale, hipStream_t st);
+hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float eps,
+                                uint8_t* q, int64_t ld_q, float* scale, hipStream_t st);
+hipError_t launch_quant_blockwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  int block_rows, int block_cols, int transpose_out, uint8_t* q,
+                                  int64_t ld_q, float* scale, hipStream_t st);
+
+// Scale application of a GEMM.
+enum class Epi : int {
+  Tensor = 0,       // out = acc * sa[0] * sb[0]
+  Row = 1,          // out = acc * sa[i] * sb[j]
+  Block128x128 = 2, // acc += P_kb * sa[kb, i] * sb[j/128, kb]   (per 128-K block)
+  Block128x1 = 3    // acc += P_kb * sa[kb, i] * sb[kb, j]
+};
+
+struct GemmProblem {
+  const uint8_t* A;
+  const uint8_t* B;
+  const float* sa;
+  const float* sb;
+  const uint16_t* bias;   // bf16 [N] ([E, N] grouped) or null
+  void* out;
+  int64_t M, N, K;
+  int64_t lda, ldb, ldo;
+  Epi epi;
+  bool b_kn;
+  bool out_bf16;
+  // grouped (MoE) problems
+  const int32_t* offsets; // device [E] end offsets, or null for a plain GEMM
+  int64_t E;
+};
+
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t st);
+
+}  // namespace fp8mm

@@ -1,0 +1,402 @@
+// Dynamic FP8 quantization kernels for gfx950.
+//
+// Per scaling group: amax -> s = fl32(amax/448) [+eps] -> code = e4m3(x / s).
+// (Per-token scaling with an epsilon: DiffSynth-Engine PR #160, "per-token
+// scaling for fp8 linear", "Highlights"; the block groupings 1x128, 128x128
+// and 128x1: pytorch PR #164141 "Add _scaled_mm_v2 API" and pytorch/ao PR
+// #2784 "improve fp8 blockwise gemm perf".)
+//
+// The pass is HBM-bound (2 bytes read + 1 byte written per element): every
+// kernel streams 16-byte loads per lane, keeps a group in registers between
+// its amax and its cast, and writes 8 bytes of codes per lane.  amax is taken
+// on the bf16 bit patterns (|x| orders like the integer x & 0x7FFF), so the
+// reductions are integer max operations and are exact and order-free.
+#include "fp8_codec.hpp"
+#include "launch.hpp"
+
+namespace fp8mm {
+namespace {
+
+struct alignas(16) U16x8 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ U16x8 load16(const uint16_t* p) {
+  return *reinterpret_cast<const U16x8*>(p);
+}
+
+// max of |x| over the 8 bf16 values, as a bf16 magnitude bit pattern.
+__device__ __forceinline__ uint32_t absmax8(const U16x8& v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = v.w[i] & 0x7FFF7FFFu;
+    m = max(m, max(a & 0xFFFFu, a >> 16));
+  }
+  return m;
+}
+
+// Elementwise |x| max of two 8-value vectors, kept as packed magnitudes.
+__device__ __forceinline__ void absmax_accum(U16x8& acc, const U16x8& v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = v.w[i] & 0x7FFF7FFFu;
+    const uint32_t lo = max(acc.w[i] & 0xFFFFu, a & 0xFFFFu);
+    const uint32_t hi = max(acc.w[i] >> 16, a >> 16);
+    acc.w[i] = lo | (hi << 16);
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Max over aligned groups of 16 lanes.
+__device__ __forceinline__ uint32_t group16_max(uint32_t v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Encode 8 bf16 values with one scale into 8 codes (little-endian bytes).
+__device__ __forceinline__ uint2 cast8(const U16x8& v, const CastScale& cs) {
+  uint32_t out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t pair = v.w[h * 2 + j];
+      const float x0 = bits_f32(pair << 16);
+      const float x1 = bits_f32(pair & 0xFFFF0000u);
+      word |= quantize_one(x0, cs) << (16 * j);
+      word |= quantize_one(x1, cs) << (16 * j + 8);
+    }
+    out[h] = word;
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Rowwise: one wave per row, the row held in registers (NIT x 512 columns).
+// ---------------------------------------------------------------------------
+template <int NIT>
+__global__ __launch_bounds__(256) void quant_rowwise_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    float eps, uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint16_t* xr = x + row * ld_x;
+  U16x8 v[NIT];
+  uint32_t m = 0;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int64_t col = (int64_t(it) * 64 + lane) * 8;
+    if (col < cols) {
+      v[it] = load16(xr + col);
+      m = max(m, absmax8(v[it]));
+    }
+  }
+  m = wave_max(m);
+  const float s = scale_from_amax(bf16_to_f32(uint16_t(m)), eps, true);
+  const CastScale cs = make_cast_scale(s);
+  if (lane == 0) scale[row] = s;
+  uint8_t* qr = q + row * ld_q;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int64_t col = (int64_t(it) * 64 + lane) * 8;
+    if (col < cols) *reinterpret_cast<uint2*>(qr + col) = cast8(v[it], cs);
+  }
+}
+
+// Rows too long for registers: amax pass, then a second (L2-resident) pass.
+__global__ __launch_bounds__(256) void quant_rowwise_long_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    float eps, uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint16_t* xr = x + row * ld_x;
+  uint32_t m = 0;
+  for (int64_t col = int64_t(lane) * 8; col < cols; col += 512) m = max(m, absmax8(load16(xr + col)));
+  m = wave_max(m);
+  const float s = scale_from_amax(bf16_to_f32(uint16_t(m)), eps, true);
+  const CastScale cs = make_cast_scale(s);
+  if (lane == 0) scale[row] = s;
+  uint8_t* qr = q + row * ld_q;
+  for (int64_t col = int64_t(lane) * 8; col < cols; col += 512)
+    *reinterpret_cast<uint2*>(qr + col) = cast8(load16(xr + col), cs);
+}
+
+// ---------------------------------------------------------------------------
+// Blockwise (1, 128): 16 lanes per group.  A workgroup owns 16 consecutive
+// rows (4 per wave, one per 16-lane group) and walks the 128-column blocks,
+// four at a time so that four loads per lane are in flight.  Scales go to
+// scale[kb * rows + row]: 16 consecutive rows -> 64 contiguous bytes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_1x128_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  if (row >= rows) return;   // whole 16-lane groups leave together
+  const int sub = lane & 15;
+  const int64_t nkb = cols / 128;
+  const uint16_t* xr = x + row * ld_x + sub * 8;
+  uint8_t* qr = q + row * ld_q + sub * 8;
+  constexpr int U = 4;
+  int64_t kb = 0;
+  for (; kb + U <= nkb; kb += U) {
+    U16x8 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load16(xr + (kb + u) * 128);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t m = group16_max(absmax8(v[u]));
+      const float s = scale_from_amax(bf16_to_f32(uint16_t(m)), 0.0f, false);
+      const CastScale cs = make_cast_scale(s);
+      if (sub == 0) scale[(kb + u) * rows + row] = s;
+      *reinterpret_cast<uint2*>(qr + (kb + u) * 128) = cast8(v[u], cs);
+    }
+  }
+  for (; kb < nkb; ++kb) {
+    const U16x8 v = load16(xr + kb * 128);
+    const uint32_t m = group16_max(absmax8(v));
+    const float s = scale_from_amax(bf16_to_f32(uint16_t(m)), 0.0f, false);
+    const CastScale cs = make_cast_scale(s);
+    if (sub == 0) scale[kb * rows + row] = s;
+    *reinterpret_cast<uint2*>(qr + kb * 128) = cast8(v, cs);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Blockwise (128, 128): one workgroup per block.  Thread t covers columns
+// (t % 16) * 8 .. +8 of rows t/16 + 16 i, i < 8.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_128x128_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale) {
+  __shared__ uint32_t wmax[4];
+  const int t = threadIdx.x;
+  const int64_t r0 = int64_t(blockIdx.y) * 128 + (t >> 4);
+  const int64_t c0 = int64_t(blockIdx.x) * 128 + (t & 15) * 8;
+  U16x8 v[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = load16(x + (r0 + 16 * i) * ld_x + c0);
+    m = max(m, absmax8(v[i]));
+  }
+  m = wave_max(m);
+  if ((t & 63) == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float s = scale_from_amax(bf16_to_f32(uint16_t(m)), 0.0f, false);
+  const CastScale cs = make_cast_scale(s);
+  if (t == 0) scale[int64_t(blockIdx.y) * (cols / 128) + blockIdx.x] = s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint2*>(q + (r0 + 16 * i) * ld_q + c0) = cast8(v[i], cs);
+}
+
+// ---------------------------------------------------------------------------
+// Blockwise (128, 1): a workgroup owns 128 rows x 128 columns; thread t holds
+// columns (t % 16) * 8 .. +8 of the 8 consecutive rows (t / 16) * 8 .. +8.
+// Column maxima: packed u16 max over the thread's rows, then across the 4
+// row groups of a wave (lane xor 16, 32), then across the 4 waves in LDS.
+// TRANSPOSE writes the codes as q[col, row]: each thread owns an 8x8 byte
+// block and stores, per column, its 8 consecutive row codes as one 8-byte
+// word.
+// ---------------------------------------------------------------------------
+template <bool TRANSPOSE>
+__global__ __launch_bounds__(256) void quant_128x1_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale) {
+  __shared__ U16x8 colmax[4][16];
+  __shared__ float col_s[128];
+  __shared__ float col_r[128];
+  const int t = threadIdx.x;
+  const int cc = t & 15;
+  const int rg = t >> 4;
+  const int64_t rb = blockIdx.y;
+  const int64_t cbase = int64_t(blockIdx.x) * 128;
+  const int64_t c0 = cbase + cc * 8;
+  const bool active = c0 < cols;          // cols % 8 == 0: all or nothing
+  const int64_t r0 = rb * 128 + rg * 8;
+  U16x8 v[8];
+  U16x8 m;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m.w[i] = 0;
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = load16(x + (r0 + i) * ld_x + c0);
+      absmax_accum(m, v[i]);
+    }
+  }
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    U16x8 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.w[i] = (uint32_t)__shfl_xor((int)m.w[i], off, 64);
+    absmax_accum(m, o);   // values are already magnitudes
+  }
+  const int wave = t >> 6;
+  if ((t & 63) < 16) colmax[wave][cc] = m;
+  __syncthreads();
+  if (t < 128) {
+    const int c = t;                       // column within the tile
+    const int chunk = c >> 3, e = c & 7;
+    uint32_t mm = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t word = colmax[w][chunk].w[e >> 1];
+      mm = max(mm, (e & 1) ? (word >> 16) : (word & 0xFFFFu));
+    }
+    const float s = scale_from_amax(bf16_to_f32(uint16_t(mm)), 0.0f, false);
+    col_s[c] = s;
+    col_r[c] = 1.0f / s;
+    if (cbase + c < cols) scale[rb * cols + cbase + c] = s;
+  }
+  __syncthreads();
+  if (!active) return;
+  CastScale cs[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    cs[j].s = col_s[cc * 8 + j];
+    cs[j].r = col_r[cc * 8 + j];
+    cs[j].fast = cs[j].s >= kFastDivMinScale;
+  }
+  if (!TRANSPOSE) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t out[2] = {0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t pair = v[i].w[j >> 1];
+        const float xv = bits_f32((j & 1) ? (pair & 0xFFFF0000u) : (pair << 16));
+        out[j >> 2] |= quantize_one(xv, cs[j]) << (8 * (j & 3));
+      }
+      *reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0) = make_uint2(out[0], out[1]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t out[2] = {0, 0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t pair = v[i].w[j >> 1];
+        const float xv = bits_f32((j & 1) ? (pair & 0xFFFF0000u) : (pair << 16));
+        out[i >> 2] |= quantize_one(xv, cs[j]) << (8 * (i & 3));
+      }
+      *reinterpret_cast<uint2*>(q + (c0 + j) * ld_q + r0) = make_uint2(out[0], out[1]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tensorwise: clear -> amax (atomic max of the float bit pattern, valid
+// because amax >= 0) -> cast -> finalize.  The scale slot holds amax until
+// the finalize kernel replaces it with the scale.
+// ---------------------------------------------------------------------------
+__global__ void tensor_clear_kernel(float* slot) { *reinterpret_cast<uint32_t*>(slot) = 0u; }
+
+__global__ __launch_bounds__(256) void tensor_amax_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x, float* slot) {
+  const int64_t chunks_per_row = cols / 8;
+  const int64_t total = rows * chunks_per_row;
+  uint32_t m = 0;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = i / chunks_per_row;
+    const int64_t c = (i - r * chunks_per_row) * 8;
+    m = max(m, absmax8(load16(x + r * ld_x + c)));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0 && m != 0)
+    atomicMax(reinterpret_cast<unsigned int*>(slot), f32_bits(bf16_to_f32(uint16_t(m))));
+}
+
+__global__ __launch_bounds__(256) void tensor_cast_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, const float* slot) {
+  const float s = scale_from_amax(*slot, 0.0f, false);
+  const CastScale cs = make_cast_scale(s);
+  const int64_t chunks_per_row = cols / 8;
+  const int64_t total = rows * chunks_per_row;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = i / chunks_per_row;
+    const int64_t c = (i - r * chunks_per_row) * 8;
+    *reinterpret_cast<uint2*>(q + r * ld_q + c) = cast8(load16(x + r * ld_x + c), cs);
+  }
+}
+
+__global__ void tensor_finalize_kernel(float* slot) { *slot = scale_from_amax(*slot, 0.0f, false); }
+
+int grid_for(int64_t work_items, int per_block, int cap) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return int(g > cap ? cap : g);
+}
+
+}  // namespace
+
+hipError_t launch_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   uint8_t* q, int64_t ld_q, float* scale, hipStream_t st) {
+  const int64_t chunks = rows * (cols / 8);
+  const int g = grid_for(chunks, 256 * 8, 2048);
+  hipLaunchKernelGGL(tensor_clear_kernel, dim3(1), dim3(1), 0, st, scale);
+  if (chunks > 0) {
+    hipLaunchKernelGGL(tensor_amax_kernel, dim3(g), dim3(256), 0, st, x, rows, cols, ld_x, scale);
+    hipLaunchKernelGGL(tensor_cast_kernel, dim3(g), dim3(256), 0, st, x, rows, cols, ld_x, q, ld_q,
+                       (const float*)scale);
+  }
+  hipLaunchKernelGGL(tensor_finalize_kernel, dim3(1), dim3(1), 0, st, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float eps,
+                                uint8_t* q, int64_t ld_q, float* scale, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid(unsigned((rows + 3) / 4)), block(256);
+  const int64_t nit = (cols + 511) / 512;
+  if (nit <= 1)
+    hipLaunchKernelGGL(quant_rowwise_kernel<1>, grid, block, 0, st, x, rows, cols, ld_x, eps, q, ld_q, scale);
+  else if (nit <= 2)
+    hipLaunchKernelGGL(quant_rowwise_kernel<2>, grid, block, 0, st, x, rows, cols, ld_x, eps, q, ld_q, scale);
+  else if (nit <= 4)
+    hipLaunchKernelGGL(quant_rowwise_kernel<4>, grid, block, 0, st, x, rows, cols, ld_x, eps, q, ld_q, scale);
+  else if (nit <= 8)
+    hipLaunchKernelGGL(quant_rowwise_kernel<8>, grid, block, 0, st, x, rows, cols, ld_x, eps, q, ld_q, scale);
+  else if (nit <= 16)
+    hipLaunchKernelGGL(quant_rowwise_kernel<16>, grid, block, 0, st, x, rows, cols, ld_x, eps, q, ld_q, scale);
+  else
+    hipLaunchKernelGGL(quant_rowwise_long_kernel, grid, block, 0, st, x, rows, cols, ld_x, eps, q, ld_q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_blockwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  int block_rows, int block_cols, int transpose_out, uint8_t* q,
+                                  int64_t ld_q, float* scale, hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  if (block_rows == 1 && block_cols == 128) {
+    hipLaunchKernelGGL(quant_1x128_kernel, dim3(unsigned((rows + 15) / 16)), dim3(256), 0, st, x, rows,
+                       cols, ld_x, q, ld_q, scale);
+  } else if (block_rows == 128 && block_cols == 128) {
+    hipLaunchKernelGGL(quant_128x128_kernel, dim3(unsigned(cols / 128), unsigned(rows / 128)), dim3(256), 0,
+                       st, x, rows, cols, ld_x, q, ld_q, scale);
+  } else {
+    const dim3 grid(unsigned((cols + 127) / 128), unsigned(rows / 128));
+    if (transpose_out)
+      hipLaunchKernelGGL(quant_128x1_kernel<true>, grid, dim3(256), 0, st, x, rows, cols, ld_x, q, ld_q, scale);
+    else
+      hipLaunchKernelGGL(quant_128x1_kernel<false>, grid, dim3(256), 0, st, x, rows, cols, ld_x, q, ld_q, scale);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp8mm

@@ -1,0 +1,277 @@
+"""GPU parity of the scaled GEMM kernels against the CPU oracle.
+
+Inputs are seeded bf16 tensors from ``workloads``; the GPU quantizes them
+with the library and the oracle quantizes them itself (the quantizers are
+bit-exact, checked in test_gpu_quant.py, so both sides multiply the same
+codes).  The GEMM bar: relative Frobenius error <= 1e-3 and elementwise
+|err| <= 4e-3 * max|ref| against the float64 oracle rounded once to the
+output dtype.  Small cases compare every element; the benchmark shapes are
+compared on sampled output entries that the oracle evaluates one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import precision_matmul_amd as fp8mm
+import workloads
+from oracle import gemm, quant
+from tests.gpu_util import TOL_FRO, TOL_MAX, bf16_dev, host, out_f64, say
+
+pytestmark = pytest.mark.gpu
+
+BLOCKS = {"1x128": (1, 128), "128x128": (128, 128), "128x1": (128, 1)}
+
+
+def _assert_close(got, ref, what):
+    rel_f, rel_m = gemm.compare(got, ref)
+    say(f"{what}: rel_fro={rel_f:.3e} rel_max={rel_m:.3e}")
+    assert np.all(np.isfinite(got)), what
+    assert rel_f <= TOL_FRO and rel_m <= TOL_MAX, (what, rel_f, rel_m)
+
+
+def _quant_both(bits, recipe, transpose_out=False):
+    """(gpu codes, gpu scales, oracle codes, oracle scales)."""
+    d = bf16_dev(bits)
+    if recipe == "tensorwise":
+        q, s = fp8mm.fp8_quantize_tensorwise(d)
+        rq, rs = quant.quantize_tensorwise(bits)
+    elif recipe == "rowwise":
+        q, s = fp8mm.fp8_quantize_rowwise(d)
+        rq, rs = quant.quantize_rowwise(bits)
+    else:
+        q, s = fp8mm.fp8_quantize_blockwise(d, BLOCKS[recipe], transpose_out=transpose_out)
+        rq, rs = quant.quantize_blockwise(bits, *BLOCKS[recipe], transpose_out=transpose_out)
+    return q, s, rq, rs
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_tensorwise_256(out_dtype):
+    inp = workloads.tensorwise()
+    qa, sa, ra, rsa = _quant_both(inp["A"], "tensorwise")
+    qb, sb, rb, rsb = _quant_both(inp["B"], "tensorwise")
+    out = fp8mm.fp8_scaled_mm(qa, qb, sa, "tensorwise", sb, "tensorwise", out_dtype=out_dtype)
+    od = "bf16" if out_dtype == torch.bfloat16 else "fp32"
+    _assert_close(out_f64(out), gemm.scaled_mm(ra, rb, rsa, "tensorwise", rsb, "tensorwise", out_dtype=od),
+                  f"tensorwise 256^3 {od}")
+
+
+def test_exact_small_integer_gemm():
+    """Codes of small integers with unit scales: the GEMM is exact in fp32."""
+    rng = np.random.default_rng(5)
+    from tests.test_oracle_gemm import _int_codes
+    a = rng.integers(-16, 17, size=(70, 256))
+    b = rng.integers(-16, 17, size=(50, 256))
+    A, B = _int_codes(a), _int_codes(b)
+    one = torch.ones((1, 1), dtype=torch.float32, device="cuda")
+    out = fp8mm.fp8_scaled_mm(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), one, "tensorwise",
+                              one, "tensorwise", out_dtype=torch.float32)
+    assert np.array_equal(out_f64(out), (a @ b.T).astype(np.float64))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 200, 4096), (17, 33, 144), (512, 640, 1040)])
+@pytest.mark.parametrize("layout", ["NK", "KN"])
+def test_tensorwise_shapes(M, N, K, layout):
+    inp = workloads.tensorwise(n=N, m=M, k=K, seed=M * 31 + N)
+    qa, sa, ra, rsa = _quant_both(inp["A"], "tensorwise")
+    if layout == "NK":
+        qb, sb, rb, rsb = _quant_both(inp["B"], "tensorwise")
+    else:
+        # B stored [K, N] with rows padded to a multiple of 16 bytes; zero
+        # padding leaves the tensorwise amax, hence the codes, unchanged.
+        bits_b = np.ascontiguousarray(inp["B"].T)
+        ldb = (N + 15) // 16 * 16
+        padded = np.zeros((K, ldb), np.uint16)
+        padded[:, :N] = bits_b
+        qpad, sb, _, _ = _quant_both(padded, "tensorwise")
+        qb = qpad[:, :N]
+        rb, rsb = quant.quantize_tensorwise(bits_b)
+        assert np.array_equal(host(qb), rb)
+    out = fp8mm.fp8_scaled_mm(qa, qb, sa, "tensorwise", sb, "tensorwise", b_layout=layout)
+    _assert_close(out_f64(out), gemm.scaled_mm(ra, rb, rsa, "tensorwise", rsb, "tensorwise", layout),
+                  f"tensorwise {M}x{N}x{K} {layout}")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 4096), (256, 512, 1024), (1, 16, 16), (129, 257, 528)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_rowwise_linear(M, N, K, with_bias):
+    inp = workloads.rowwise(M=M, N=N, K=K, seed=M + N + K)
+    qa, sa, ra, rsa = _quant_both(inp["x"], "rowwise")
+    qb, sb, rb, rsb = _quant_both(inp["w"], "rowwise")
+    bias = bf16_dev(inp["bias"]) if with_bias else None
+    rbias = quant.bf16_to_f32(inp["bias"]) if with_bias else None
+    out = fp8mm.fp8_scaled_mm(qa, qb, sa, "rowwise", sb, "rowwise", bias=bias)
+    _assert_close(out_f64(out), gemm.scaled_mm(ra, rb, rsa, "rowwise", rsb, "rowwise", bias=rbias),
+                  f"rowwise {M}x{N}x{K} bias={with_bias}")
+    fwd = fp8mm.fp8_linear_forward(qa, sa, "rowwise", qb, sb, "rowwise", bias=bias)
+    assert torch.equal(fwd, out)
+
+
+@pytest.mark.parametrize("M,N,K", [(320, 384, 1024), (256, 256, 128), (1000, 128, 512), (64, 640, 2048)])
+def test_blockwise_forward(M, N, K):
+    inp = workloads.blockwise(M=M, N=N, K=K, seed=M + 3 * N + K)
+    qa, sa, ra, rsa = _quant_both(inp["input"], "1x128")
+    qb, sb, rb, rsb = _quant_both(inp["weight"], "128x128")
+    out = fp8mm.fp8_linear_forward(qa, sa, "1x128", qb, sb, "128x128")
+    _assert_close(out_f64(out), gemm.linear_forward(ra, rsa, "1x128", rb, rsb, "128x128"),
+                  f"blockwise fwd {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N_out,K_in", [(320, 512, 384), (256, 128, 256), (130, 256, 640)])
+def test_blockwise_grad_input(M, N_out, K_in):
+    inp = workloads.blockwise(M=M, N=N_out, K=K_in, seed=M + N_out + 5 * K_in)
+    qg, sg, rg, rsg = _quant_both(inp["grad_output"], "1x128")      # [M, N_out]
+    qw, sw, rw, rsw = _quant_both(inp["weight"], "128x128")          # [N_out, K_in]
+    out = fp8mm.fp8_linear_grad_input(qg, sg, "1x128", qw, sw, "128x128")
+    _assert_close(out_f64(out), gemm.linear_grad_input(rg, rsg, "1x128", rw, rsw, "128x128"),
+                  f"blockwise grad_input {M}x{K_in}x{N_out}")
+
+
+@pytest.mark.parametrize("T,N_out,K_in", [(512, 256, 384), (256, 128, 128), (384, 80, 176)])
+def test_blockwise_grad_weight(T, N_out, K_in):
+    inp = workloads.grad_weight(T=T, N_out=N_out, K_in=K_in, seed=T + N_out + K_in)
+    qg, sg, rg, rsg = _quant_both(inp["grad_output"], "128x1", transpose_out=True)   # [N_out, T]
+    qx, sx, rx, rsx = _quant_both(inp["input"], "128x1", transpose_out=True)         # [K_in, T]
+    out = fp8mm.fp8_linear_grad_weight(qg, sg, qx, sx)
+    _assert_close(out_f64(out), gemm.linear_grad_weight(rg, rsg, rx, rsx),
+                  f"blockwise grad_weight {N_out}x{K_in}x{T}")
+
+
+def _grouped_case(E, N, K, sizes, seed):
+    g = workloads.streams(seed, 2)
+    M = int(np.sum(sizes))
+    act = workloads.normal_bf16(g[0], (M + 7, K))          # 7 trailing rows no expert owns
+    W = workloads.normal_bf16(g[1], (E, N, K), 0.02)
+    offs = np.cumsum(sizes).astype(np.int32)
+    qa, sa, ra, rsa = _quant_both(act, "rowwise")
+    qw, sw, rw, rsw = _quant_both(W.reshape(E * N, K), "rowwise")
+    out = fp8mm.fp8_scaled_grouped_mm(qa, qw.reshape(E, N, K), torch.from_numpy(offs).cuda(), sa,
+                                      sw.reshape(E, N))
+    ref, written = gemm.grouped_mm(ra, rw.reshape(E, N, K), offs, rsa, rsw.reshape(E, N))
+    got = out_f64(out)
+    assert np.all(got[~written] == 0), "rows no expert owns must not be written"
+    return got[written], ref[written]
+
+
+@pytest.mark.parametrize("E,N,K,sizes", [
+    (8, 256, 512, [100, 0, 300, 1, 129, 0, 0, 256]),
+    (3, 136, 272, [5, 260, 64]),
+    (1, 128, 256, [333]),
+    (70, 64, 128, [3] * 70)])
+def test_grouped_rowwise(E, N, K, sizes):
+    got, ref = _grouped_case(E, N, K, np.array(sizes), seed=E + N + K)
+    _assert_close(got, ref, f"grouped E={E} N={N} K={K}")
+
+
+def test_grouped_single_expert_equals_rowwise_gemm():
+    inp = workloads.rowwise(M=200, N=128, K=256, seed=77)
+    qa, sa, _, _ = _quant_both(inp["x"], "rowwise")
+    qb, sb, _, _ = _quant_both(inp["w"], "rowwise")
+    grouped = fp8mm.fp8_scaled_grouped_mm(qa, qb.reshape(1, 128, 256), torch.tensor([200], dtype=torch.int32,
+                                          device="cuda"), sa, sb)
+    plain = fp8mm.fp8_scaled_mm(qa, qb, sa, "rowwise", sb, "rowwise")
+    _assert_close(out_f64(grouped), out_f64(plain), "grouped E=1 vs rowwise")
+
+
+def test_zero_sized_problems():
+    dev = "cuda"
+    z = torch.empty((0, 128), dtype=torch.uint8, device=dev)
+    b = torch.zeros((64, 128), dtype=torch.uint8, device=dev)
+    one = torch.ones((1, 1), dtype=torch.float32, device=dev)
+    out = fp8mm.fp8_scaled_mm(z, b, one, "tensorwise", one, "tensorwise")
+    assert out.shape == (0, 64)
+    a = torch.zeros((8, 0), dtype=torch.uint8, device=dev)
+    bb = torch.zeros((4, 0), dtype=torch.uint8, device=dev)
+    out = fp8mm.fp8_scaled_mm(a, bb, one, "tensorwise", one, "tensorwise", out_dtype=torch.float32)
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_unsupported_pair_raises_not_implemented():
+    a = torch.zeros((128, 128), dtype=torch.uint8, device="cuda")
+    s = torch.ones((128, 1), dtype=torch.float32, device="cuda")
+    with pytest.raises(NotImplementedError):
+        fp8mm.fp8_scaled_mm(a, a, s, "rowwise", torch.ones((1, 1), device="cuda"), "tensorwise")
+
+
+# ---- benchmark shapes: full-size launches, sampled outputs ----
+
+def _sample(n, count, seed):
+    return np.sort(np.random.default_rng(seed).choice(n, count, replace=False))
+
+
+def test_full_rowwise_linear_sampled():
+    inp = workloads.rowwise()
+    x, w, bias = inp["x"], inp["w"], inp["bias"]
+    qa, sa = fp8mm.fp8_quantize_rowwise(bf16_dev(x))
+    qb, sb = fp8mm.fp8_quantize_rowwise(bf16_dev(w))
+    out = fp8mm.fp8_scaled_mm(qa, qb, sa, "rowwise", sb, "rowwise", bias=bf16_dev(bias))
+    got = out_f64(out)
+    I, J = _sample(x.shape[0], 64, 1), _sample(w.shape[0], 64, 2)
+    ra, rsa = quant.quantize_rowwise(x[I])
+    rb, rsb = quant.quantize_rowwise(w[J])
+    ref = gemm.scaled_mm(ra, rb, rsa, "rowwise", rsb, "rowwise", bias=quant.bf16_to_f32(bias[J]))
+    _assert_close(got[np.ix_(I, J)], ref, "rowwise 8192x4096x4096 sampled")
+
+
+@pytest.mark.parametrize("M,N,K", [(16640, 5120, 8192), (16640, 8192, 5120)])
+def test_full_blockwise_forward_and_grad_input_sampled(M, N, K):
+    inp = workloads.blockwise(M=M, N=N, K=K)
+    x, w, go = inp["input"], inp["weight"], inp["grad_output"]
+    qx, sx = fp8mm.fp8_quantize_blockwise(bf16_dev(x), (1, 128))
+    qw, sw = fp8mm.fp8_quantize_blockwise(bf16_dev(w), (128, 128))
+    fwd = out_f64(fp8mm.fp8_linear_forward(qx, sx, "1x128", qw, sw, "128x128"))
+    I = _sample(M, 48, 3)
+    slabs = _sample(N // 128, 3, 4)
+    J = np.concatenate([s * 128 + _sample(128, 16, 5 + s) for s in slabs])
+    rqx, rsx = quant.quantize_blockwise(x[I], 1, 128)
+    # evaluate per slab with the slab's scale row (columns of a slab share one 128-row block)
+    ref = np.zeros((len(I), len(J)))
+    for t, s in enumerate(slabs):
+        q, sc = quant.quantize_blockwise(w[s * 128:(s + 1) * 128], 128, 128)
+        cols = J[t * 16:(t + 1) * 16] - s * 128
+        full = gemm.scaled_mm(rqx, q, rsx, "1x128", sc, "128x128")   # [len(I), 128]
+        ref[:, t * 16:(t + 1) * 16] = full[:, cols]
+    _assert_close(fwd[np.ix_(I, J)], ref, f"blockwise fwd {M}x{N}x{K} sampled")
+    # grad_input = grad_output @ weight, with grad_output [M, N] and weight [N, K]
+    qg, sg = fp8mm.fp8_quantize_blockwise(bf16_dev(go), (1, 128))
+    gi = out_f64(fp8mm.fp8_linear_grad_input(qg, sg, "1x128", qw, sw, "128x128"))
+    Jk = _sample(K, 48, 6)
+    rqg, rsg = quant.quantize_blockwise(go[I], 1, 128)
+    rqw_full, rsw_full = quant.quantize_blockwise(w, 128, 128)
+    ref_gi = gemm.scaled_mm_entries(rqg, rqw_full, rsg, "1x128", rsw_full, "128x128",
+                                    np.repeat(np.arange(len(I)), len(Jk)), np.tile(Jk, len(I)), layout="KN")
+    _assert_close(gi[np.ix_(I, Jk)].reshape(-1), ref_gi, f"blockwise grad_input {M}x{K}x{N} sampled")
+
+
+def test_full_blockwise_grad_weight_sampled():
+    inp = workloads.grad_weight()
+    go, x = inp["grad_output"], inp["input"]                # [T, N_out], [T, K_in]
+    qg, sg = fp8mm.fp8_quantize_blockwise(bf16_dev(go), (128, 1), transpose_out=True)
+    qx, sx = fp8mm.fp8_quantize_blockwise(bf16_dev(x), (128, 1), transpose_out=True)
+    gw = out_f64(fp8mm.fp8_linear_grad_weight(qg, sg, qx, sx))
+    I, J = _sample(go.shape[1], 48, 7), _sample(x.shape[1], 48, 8)
+    rqg, rsg = quant.quantize_blockwise(np.ascontiguousarray(go[:, I]), 128, 1, transpose_out=True)
+    rqx, rsx = quant.quantize_blockwise(np.ascontiguousarray(x[:, J]), 128, 1, transpose_out=True)
+    ref = gemm.linear_grad_weight(rqg, rsg, rqx, rsx)
+    _assert_close(gw[np.ix_(I, J)], ref, "blockwise grad_weight 5120x8192x16640 sampled")
+
+
+def test_full_grouped_moe_sampled():
+    inp = workloads.grouped()
+    act, W, offs = inp["act"], inp["W"], inp["offs"]
+    E, N, K = W.shape
+    qa, sa = fp8mm.fp8_quantize_rowwise(bf16_dev(act))
+    qw, sw = fp8mm.fp8_quantize_rowwise(bf16_dev(W.reshape(E * N, K)))
+    out = out_f64(fp8mm.fp8_scaled_grouped_mm(qa, qw.reshape(E, N, K), torch.from_numpy(offs).cuda(), sa,
+                                              sw.reshape(E, N)))
+    assert offs[-1] == act.shape[0]
+    rows = _sample(act.shape[0], 96, 9)
+    cols = _sample(N, 64, 10)
+    expert = np.searchsorted(offs, rows, side="right")
+    ra, rsa = quant.quantize_rowwise(act[rows])
+    got, ref = [], []
+    for t, (r, e) in enumerate(zip(rows, expert)):
+        rw, rsw = quant.quantize_rowwise(W[e][cols])
+        ref.append(gemm.scaled_mm(ra[t:t + 1], rw, rsa[t:t + 1], "rowwise", rsw, "rowwise")[0])
+        got.append(out[r, cols])
+    _assert_close(np.array(got), np.array(ref), "grouped E=64 16384x1408x2048 sampled")

@@ -1,0 +1,167 @@
+"""GPU parity of the quantization kernels: codes and scales bit-exact against
+the CPU oracle, through the C ABI (Python binding)."""
+
+import numpy as np
+import pytest
+import torch
+
+import precision_matmul_amd as fp8mm
+import workloads
+from oracle import e4m3, quant
+from tests.gpu_util import bf16_dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(q_gpu, s_gpu, q_ref, s_ref, what):
+    qg, sg = host(q_gpu), host(s_gpu)
+    assert qg.shape == q_ref.shape, (what, qg.shape, q_ref.shape)
+    assert sg.reshape(-1).shape == s_ref.reshape(-1).shape, (what, sg.shape, s_ref.shape)
+    bad_s = np.flatnonzero(sg.reshape(-1).view(np.uint32) != s_ref.reshape(-1).view(np.uint32))
+    assert bad_s.size == 0, (what, "scales differ at", bad_s[:8], sg.reshape(-1)[bad_s[:4]], s_ref.reshape(-1)[bad_s[:4]])
+    bad = np.argwhere(qg != q_ref)
+    assert bad.size == 0, (what, "codes differ at", bad[:8], qg[tuple(bad[0])], q_ref[tuple(bad[0])])
+
+
+def _special_rows(ncols):
+    """Rows whose amax is 448 (scale exactly 1): every E4M3 midpoint, its bf16
+    neighbours and the subnormal range pass through the cast unchanged."""
+    t = e4m3.decode_table()[:0x7F]
+    mids = (t[:-1] + t[1:]) / 2
+    vals = np.concatenate([mids, t, np.array([2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11, 1e-30, 0.0])])
+    v32 = vals.astype(np.float32)
+    bits = workloads.f32_to_bf16_bits(v32).astype(np.int32)
+    cand = np.concatenate([bits, bits + 1, bits - 1, bits | 0x8000])
+    cand = cand[(cand >= 0) & (cand < 0x10000)].astype(np.uint16)
+    mag = quant.bf16_to_f32(cand)
+    cand = cand[np.isfinite(mag) & (np.abs(mag) <= 448.0)]
+    rows = []
+    for i in range(0, cand.size, ncols - 1):
+        chunk = cand[i:i + ncols - 1]
+        row = np.zeros(ncols, np.uint16)
+        row[:chunk.size] = chunk
+        row[-1] = workloads.f32_to_bf16_bits(np.array([448.0], np.float32))[0]
+        rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("rows,cols", [(8, 4096), (37, 1040), (5, 16), (3, 8704), (64, 8192)])
+def test_rowwise_bitexact(rows, cols):
+    say(f"rowwise {rows}x{cols}")
+    x = workloads.rowwise(M=rows, N=16, K=cols)["x"]
+    q, s = fp8mm.fp8_quantize_rowwise(bf16_dev(x))
+    rq, rs = quant.quantize_rowwise(x)
+    _check(q, s, rq, rs, f"rowwise {rows}x{cols}")
+
+
+def test_rowwise_midpoints_ties_subnormals_and_tiny_rows():
+    x = _special_rows(512)
+    tiny = workloads.f32_to_bf16_bits(np.array([[1e-9] * 512, [0.0] * 512, [-3e-38] * 512], np.float32))
+    x = np.concatenate([x, tiny, (x[:2] | 0x8000).astype(np.uint16)])
+    q, s = fp8mm.fp8_quantize_rowwise(bf16_dev(x))
+    rq, rs = quant.quantize_rowwise(x)
+    _check(q, s, rq, rs, "rowwise specials")
+    q, s = fp8mm.fp8_quantize_rowwise(bf16_dev(x), eps=0.0)
+    rq, rs = quant.quantize_rowwise(x, eps=0.0)
+    _check(q, s, rq, rs, "rowwise specials eps=0")
+
+
+@pytest.mark.parametrize("rows,cols", [(256, 256), (100, 48), (1, 16), (384, 1024)])
+def test_tensorwise_bitexact(rows, cols):
+    say(f"tensorwise {rows}x{cols}")
+    x = workloads.tensorwise(n=cols, m=rows, k=cols)["A"][:rows, :cols]
+    q, s = fp8mm.fp8_quantize_tensorwise(bf16_dev(x))
+    rq, rs = quant.quantize_tensorwise(x)
+    _check(q, s, rq, rs, f"tensorwise {rows}x{cols}")
+
+
+def test_tensorwise_specials_tiny_scale_and_empty():
+    x = _special_rows(256)
+    q, s = fp8mm.fp8_quantize_tensorwise(bf16_dev(x))
+    rq, rs = quant.quantize_tensorwise(x)
+    _check(q, s, rq, rs, "tensorwise specials")
+    # amax ~1e-30: the scale is below 2^-90 and takes the plain division path
+    rng = np.random.default_rng(3)
+    tiny = workloads.f32_to_bf16_bits((rng.standard_normal((64, 128)) * 1e-30).astype(np.float32))
+    q, s = fp8mm.fp8_quantize_tensorwise(bf16_dev(tiny))
+    rq, rs = quant.quantize_tensorwise(tiny)
+    _check(q, s, rq, rs, "tensorwise tiny")
+    z = np.zeros((32, 64), np.uint16)
+    z[3:] = 0x8000
+    q, s = fp8mm.fp8_quantize_tensorwise(bf16_dev(z))
+    rq, rs = quant.quantize_tensorwise(z)
+    _check(q, s, rq, rs, "tensorwise zeros")
+    q, s = fp8mm.fp8_quantize_tensorwise(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"))
+    assert q.shape == (0, 64) and host(s).reshape(-1)[0] == 1.0
+
+
+@pytest.mark.parametrize("block,rows,cols", [
+    ((1, 128), 257, 1024), ((1, 128), 16, 128), ((1, 128), 33, 640),
+    ((128, 128), 384, 512), ((128, 128), 128, 128),
+    ((128, 1), 256, 384), ((128, 1), 128, 144), ((128, 1), 384, 16)])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_blockwise_bitexact(block, rows, cols, transpose):
+    if transpose and block != (128, 1):
+        pytest.skip("transpose_out is defined for (128, 1) only")
+    say(f"blockwise {block} {rows}x{cols} T={transpose}")
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = workloads.f32_to_bf16_bits((rng.standard_normal((rows, cols)) *
+                                    np.exp2(rng.integers(-20, 20, size=(rows, 1)))).astype(np.float32))
+    q, s = fp8mm.fp8_quantize_blockwise(bf16_dev(x), block, transpose_out=transpose)
+    rq, rs = quant.quantize_blockwise(x, block[0], block[1], transpose_out=transpose)
+    _check(q, s, rq, rs, f"blockwise {block} {rows}x{cols} T={transpose}")
+
+
+def test_blockwise_specials():
+    x = _special_rows(128)
+    x = np.concatenate([x, np.zeros(((-x.shape[0]) % 128, 128), np.uint16)])
+    for block in ((1, 128), (128, 128), (128, 1)):
+        q, s = fp8mm.fp8_quantize_blockwise(bf16_dev(x), block)
+        rq, rs = quant.quantize_blockwise(x, *block)
+        _check(q, s, rq, rs, f"specials {block}")
+
+
+def test_quantize_is_deterministic_across_runs():
+    x = workloads.blockwise(M=512, N=128, K=2048)["input"]
+    xd = bf16_dev(x)
+    q1, s1 = fp8mm.fp8_quantize_tensorwise(xd)
+    q2, s2 = fp8mm.fp8_quantize_tensorwise(xd)
+    assert np.array_equal(host(q1), host(q2)) and np.array_equal(host(s1), host(s2))
+
+
+# ---- the benchmark shapes, checked on sampled rows / blocks / columns ----
+
+def test_full_size_activation_1x128_sampled_rows():
+    x = workloads.blockwise()["input"]                     # [16640, 8192]
+    q, s = fp8mm.fp8_quantize_blockwise(bf16_dev(x), (1, 128))
+    qh, sh = host(q), host(s)
+    rows = np.random.default_rng(0).choice(x.shape[0], 48, replace=False)
+    rq, rs = quant.quantize_blockwise(x[rows], 1, 128)
+    assert np.array_equal(qh[rows], rq) and np.array_equal(sh[:, rows], rs)
+
+
+def test_full_size_weight_128x128_sampled_slabs():
+    w = workloads.blockwise()["weight"]                    # [5120, 8192]
+    q, s = fp8mm.fp8_quantize_blockwise(bf16_dev(w), (128, 128))
+    qh, sh = host(q), host(s)
+    for slab in (0, 17, 39):
+        rq, rs = quant.quantize_blockwise(w[slab * 128:(slab + 1) * 128], 128, 128)
+        assert np.array_equal(qh[slab * 128:(slab + 1) * 128], rq) and np.array_equal(sh[slab], rs[0])
+
+
+def test_full_size_grad_weight_operand_128x1_sampled_columns():
+    g = workloads.grad_weight()["grad_output"]             # [16640, 5120]
+    q, s = fp8mm.fp8_quantize_blockwise(bf16_dev(g), (128, 1), transpose_out=True)
+    qh, sh = host(q), host(s)
+    cols = np.random.default_rng(1).choice(g.shape[1], 40, replace=False)
+    rq, rs = quant.quantize_blockwise(np.ascontiguousarray(g[:, cols]), 128, 1, transpose_out=True)
+    assert np.array_equal(qh[cols], rq) and np.array_equal(sh[:, cols], rs)
+
+
+def test_full_size_rowwise_moe_weights_sampled_rows():
+    W = workloads.grouped()["W"].reshape(64 * 1408, 2048)
+    q, s = fp8mm.fp8_quantize_rowwise(bf16_dev(W))
+    qh, sh = host(q), host(s)
+    rows = np.random.default_rng(2).choice(W.shape[0], 256, replace=False)
+    rq, rs = quant.quantize_rowwise(W[rows])
+    assert np.array_equal(qh[rows], rq) and np.array_equal(sh[rows, 0], rs)

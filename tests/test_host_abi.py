@@ -1,0 +1,138 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+
+Every call below is made with arguments that fail validation, so nothing is
+ever enqueued (fake non-null pointers are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from precision_matmul_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8mm.h")
+FAKE = 0x1000          # 16-byte aligned, never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8_\w+|fp8mm_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libfp8mm.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_recipe_pair_table(lib):
+    R = _lib.RECIPES
+    ok = {("tensorwise", "tensorwise"), ("rowwise", "rowwise"), ("1x128", "128x128"), ("1x128", "128x1")}
+    for a in R:
+        for b in R:
+            for layout in (0, 1):
+                assert lib.fp8mm_recipe_pair_supported(R[a], R[b], layout) == int((a, b) in ok), (a, b)
+    assert lib.fp8mm_recipe_pair_supported(0, 0, 7) == 0
+
+
+def _mm(lib, **kw):
+    a = dict(A=FAKE, M=64, K=256, lda=256, B=FAKE, N=64, ldb=256, layout=0, sa=FAKE, ra=0, sb=FAKE, rb=0,
+             bias=None, od=0, out=FAKE, ldo=64, st=None)
+    a.update(kw)
+    return lib.fp8_scaled_mm(a["A"], a["M"], a["K"], a["lda"], a["B"], a["N"], a["ldb"], a["layout"], a["sa"],
+                             a["ra"], a["sb"], a["rb"], a["bias"], a["od"], a["out"], a["ldo"], a["st"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), _lib.EINVAL),
+    (dict(out=None), _lib.EINVAL),
+    (dict(sb=None), _lib.EINVAL),
+    (dict(M=-1), _lib.EINVAL),
+    (dict(K=100, lda=112, ldb=112), _lib.EINVAL),                 # K % 16
+    (dict(lda=128), _lib.EINVAL),                                  # lda < K
+    (dict(lda=264), _lib.EINVAL),                                  # lda % 16
+    (dict(ldb=200), _lib.EINVAL),
+    (dict(ldo=32), _lib.EINVAL),
+    (dict(A=FAKE + 8), _lib.EINVAL),                               # alignment
+    (dict(ra=9), _lib.EINVAL),                                     # unknown enum
+    (dict(layout=3), _lib.EINVAL),
+    (dict(od=5), _lib.EINVAL),
+    (dict(ra=1, rb=0), _lib.ENOTIMPL),                             # rowwise x tensorwise
+    (dict(ra=3, rb=2), _lib.ENOTIMPL),                             # 128x128 x 1x128
+    (dict(ra=2, rb=3, K=144, lda=144, ldb=144), _lib.EINVAL),      # blockwise K % 128
+    (dict(ra=2, rb=3, N=100, ldo=100), _lib.EINVAL),               # 128x128 needs N % 128
+    (dict(ra=0, rb=0, layout=1, ldb=32), _lib.EINVAL),             # KN: ldb >= N
+])
+def test_scaled_mm_rejects_before_launch(lib, kw, code):
+    assert _mm(lib, **kw) == code
+    assert lib.fp8mm_last_error().decode()
+
+
+def test_status_maps_to_python_exceptions(lib):
+    assert _mm(lib, ra=1, rb=0) == _lib.ENOTIMPL
+    with pytest.raises(NotImplementedError):
+        _lib.check(_lib.ENOTIMPL, "x")
+    with pytest.raises(ValueError):
+        _lib.check(_lib.EINVAL, "x")
+    with pytest.raises(RuntimeError):
+        _lib.check(_lib.ERUNTIME, "x")
+
+
+def test_grouped_requires_offsets_and_checks_shapes(lib):
+    f = lib.fp8_scaled_grouped_mm
+    # A, M_total, K, B, E, N, offsets, sa, sb, bias, od, out, ldo, stream
+    assert f(FAKE, 64, 256, FAKE, 4, 64, None, FAKE, FAKE, None, 0, FAKE, 64, None) == _lib.EINVAL
+    assert "offsets" in lib.fp8mm_last_error().decode()
+    assert f(FAKE, 64, 100, FAKE, 4, 64, FAKE, FAKE, FAKE, None, 0, FAKE, 64, None) == _lib.EINVAL
+    assert f(FAKE, 64, 256, FAKE, -1, 64, FAKE, FAKE, FAKE, None, 0, FAKE, 64, None) == _lib.EINVAL
+    assert f(FAKE, 64, 256, FAKE, 4, 64, FAKE, FAKE, FAKE, None, 0, FAKE, 32, None) == _lib.EINVAL
+    assert f(FAKE, 64, 256, FAKE, 4, 64, FAKE, FAKE, FAKE, None, 9, FAKE, 64, None) == _lib.EINVAL
+
+
+def test_quantizers_reject_before_launch(lib):
+    # x, rows, cols, ld_x, q, ld_q, scale, stream
+    assert lib.fp8_quantize_tensorwise(None, 4, 16, 16, FAKE, 16, FAKE, None) == _lib.EINVAL
+    assert lib.fp8_quantize_tensorwise(FAKE, 4, 20, 24, FAKE, 32, FAKE, None) == _lib.EINVAL   # cols % 16
+    assert lib.fp8_quantize_tensorwise(FAKE, 4, 16, 12, FAKE, 16, FAKE, None) == _lib.EINVAL   # ld_x < cols
+    assert lib.fp8_quantize_tensorwise(FAKE, 4, 16, 16, FAKE, 8, FAKE, None) == _lib.EINVAL    # ld_q
+    assert lib.fp8_quantize_rowwise(FAKE, 4, 16, 16, ctypes.c_float(-1.0), FAKE, 16, FAKE, None) == _lib.EINVAL
+    assert lib.fp8_quantize_rowwise(FAKE, 4, 16, 16, ctypes.c_float(float("nan")), FAKE, 16, FAKE, None) == _lib.EINVAL
+    qb = lib.fp8_quantize_blockwise
+    # x, rows, cols, ld_x, br, bc, transpose, q, ld_q, scale, stream
+    assert qb(FAKE, 128, 128, 128, 64, 64, 0, FAKE, 128, FAKE, None) == _lib.ENOTIMPL
+    assert qb(FAKE, 128, 128, 128, 1, 128, 1, FAKE, 128, FAKE, None) == _lib.ENOTIMPL          # transpose only 128x1
+    assert qb(FAKE, 100, 128, 128, 128, 128, 0, FAKE, 128, FAKE, None) == _lib.EINVAL          # rows % 128
+    assert qb(FAKE, 128, 144, 144, 1, 128, 0, FAKE, 144, FAKE, None) == _lib.EINVAL            # cols % 128
+    assert qb(FAKE, 256, 64, 64, 128, 1, 1, FAKE, 128, FAKE, None) == _lib.EINVAL              # ld_q < rows (T)
+    assert qb(FAKE, 256, 64, 64, 128, 1, 2, FAKE, 256, FAKE, None) == _lib.EINVAL              # transpose flag
+
+
+def test_call_forms_validate_through_scaled_mm(lib):
+    # grad_input with K_in not a multiple of 128 under 128x128 weights -> EINVAL
+    assert lib.fp8_linear_grad_input(FAKE, 64, 256, FAKE, 2, FAKE, 200, FAKE, 3, 0, FAKE, None) == _lib.EINVAL
+    # grad_weight with T not a multiple of 128 -> EINVAL
+    assert lib.fp8_linear_grad_weight(FAKE, 64, 200, FAKE, FAKE, 64, FAKE, 0, FAKE, None) == _lib.EINVAL
+    # forward with an unsupported pair -> ENOTIMPL
+    assert lib.fp8_linear_forward(FAKE, 64, 256, FAKE, 2, FAKE, 64, FAKE, 1, None, 0, FAKE, None) == _lib.ENOTIMPL
+
+
+def test_product_path_does_not_reference_the_oracle():
+    pkg = os.path.join(ROOT, "precision_matmul_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("the oracle", ""), f
