@@ -104,6 +104,9 @@ def round_bf16(x):
 
 
 def round_out(x, out_dtype):
+    """Round once to out_dtype; out_dtype None keeps the float64 value."""
+    if out_dtype is None:
+        return np.asarray(x, np.float64)
     if out_dtype == "bf16":
         return round_bf16(x)
     if out_dtype == "fp32":
@@ -197,6 +200,22 @@ def linear_grad_weight(gt_q, gt_scale, xt_q, xt_scale, out_dtype="bf16"):
     orientation, scale [T/128, K_in]), layout NK."""
     return scaled_mm(gt_q, xt_q, gt_scale, "1x128", xt_scale, "128x1", "NK",
                      None, out_dtype)
+
+
+def parity(out, ref_exact, out_dtype="bf16"):
+    """The GEMM parity figures of a result against the float64 oracle:
+      rel_fro = ||out - R|| / ||R||, R = ref_exact rounded once to out_dtype
+      rel_max = max|out - ref_exact| / max|ref_exact|
+    The Frobenius figure uses the rounded reference because bf16 rounding
+    alone is about 1.6e-3 relative in Frobenius norm; the elementwise figure
+    uses the unrounded reference because one correct bf16 rounding moves an
+    element by at most 2^-8 of its own magnitude, while against the rounded
+    reference a single last-place flip can reach 2^-7."""
+    out = np.asarray(out, np.float64)
+    ref_exact = np.asarray(ref_exact, np.float64)
+    rel_f, _ = compare(out, round_out(ref_exact, out_dtype))
+    _, rel_m = compare(out, ref_exact)
+    return rel_f, rel_m
 
 
 def compare(out, ref):

@@ -23,8 +23,10 @@ pytestmark = pytest.mark.gpu
 BLOCKS = {"1x128": (1, 128), "128x128": (128, 128), "128x1": (128, 1)}
 
 
-def _assert_close(got, ref, what):
-    rel_f, rel_m = gemm.compare(got, ref)
+def _assert_close(got, ref_exact, what, out_dtype="bf16"):
+    """ref_exact: the unrounded float64 oracle (gemm.parity rounds it once to
+    out_dtype for the Frobenius figure)."""
+    rel_f, rel_m = gemm.parity(got, ref_exact, out_dtype)
     say(f"{what}: rel_fro={rel_f:.3e} rel_max={rel_m:.3e}")
     assert np.all(np.isfinite(got)), what
     assert rel_f <= TOL_FRO and rel_m <= TOL_MAX, (what, rel_f, rel_m)
@@ -52,8 +54,8 @@ def test_tensorwise_256(out_dtype):
     qb, sb, rb, rsb = _quant_both(inp["B"], "tensorwise")
     out = fp8mm.fp8_scaled_mm(qa, qb, sa, "tensorwise", sb, "tensorwise", out_dtype=out_dtype)
     od = "bf16" if out_dtype == torch.bfloat16 else "fp32"
-    _assert_close(out_f64(out), gemm.scaled_mm(ra, rb, rsa, "tensorwise", rsb, "tensorwise", out_dtype=od),
-                  f"tensorwise 256^3 {od}")
+    _assert_close(out_f64(out), gemm.scaled_mm(ra, rb, rsa, "tensorwise", rsb, "tensorwise", out_dtype=None),
+                  f"tensorwise 256^3 {od}", out_dtype=od)
 
 
 def test_exact_small_integer_gemm():
@@ -88,7 +90,7 @@ def test_tensorwise_shapes(M, N, K, layout):
         rb, rsb = quant.quantize_tensorwise(bits_b)
         assert np.array_equal(host(qb), rb)
     out = fp8mm.fp8_scaled_mm(qa, qb, sa, "tensorwise", sb, "tensorwise", b_layout=layout)
-    _assert_close(out_f64(out), gemm.scaled_mm(ra, rb, rsa, "tensorwise", rsb, "tensorwise", layout),
+    _assert_close(out_f64(out), gemm.scaled_mm(ra, rb, rsa, "tensorwise", rsb, "tensorwise", layout, out_dtype=None),
                   f"tensorwise {M}x{N}x{K} {layout}")
 
 
@@ -101,7 +103,7 @@ def test_rowwise_linear(M, N, K, with_bias):
     bias = bf16_dev(inp["bias"]) if with_bias else None
     rbias = quant.bf16_to_f32(inp["bias"]) if with_bias else None
     out = fp8mm.fp8_scaled_mm(qa, qb, sa, "rowwise", sb, "rowwise", bias=bias)
-    _assert_close(out_f64(out), gemm.scaled_mm(ra, rb, rsa, "rowwise", rsb, "rowwise", bias=rbias),
+    _assert_close(out_f64(out), gemm.scaled_mm(ra, rb, rsa, "rowwise", rsb, "rowwise", bias=rbias, out_dtype=None),
                   f"rowwise {M}x{N}x{K} bias={with_bias}")
     fwd = fp8mm.fp8_linear_forward(qa, sa, "rowwise", qb, sb, "rowwise", bias=bias)
     assert torch.equal(fwd, out)
@@ -113,7 +115,7 @@ def test_blockwise_forward(M, N, K):
     qa, sa, ra, rsa = _quant_both(inp["input"], "1x128")
     qb, sb, rb, rsb = _quant_both(inp["weight"], "128x128")
     out = fp8mm.fp8_linear_forward(qa, sa, "1x128", qb, sb, "128x128")
-    _assert_close(out_f64(out), gemm.linear_forward(ra, rsa, "1x128", rb, rsb, "128x128"),
+    _assert_close(out_f64(out), gemm.linear_forward(ra, rsa, "1x128", rb, rsb, "128x128", out_dtype=None),
                   f"blockwise fwd {M}x{N}x{K}")
 
 
@@ -123,7 +125,7 @@ def test_blockwise_grad_input(M, N_out, K_in):
     qg, sg, rg, rsg = _quant_both(inp["grad_output"], "1x128")      # [M, N_out]
     qw, sw, rw, rsw = _quant_both(inp["weight"], "128x128")          # [N_out, K_in]
     out = fp8mm.fp8_linear_grad_input(qg, sg, "1x128", qw, sw, "128x128")
-    _assert_close(out_f64(out), gemm.linear_grad_input(rg, rsg, "1x128", rw, rsw, "128x128"),
+    _assert_close(out_f64(out), gemm.linear_grad_input(rg, rsg, "1x128", rw, rsw, "128x128", out_dtype=None),
                   f"blockwise grad_input {M}x{K_in}x{N_out}")
 
 
@@ -133,7 +135,7 @@ def test_blockwise_grad_weight(T, N_out, K_in):
     qg, sg, rg, rsg = _quant_both(inp["grad_output"], "128x1", transpose_out=True)   # [N_out, T]
     qx, sx, rx, rsx = _quant_both(inp["input"], "128x1", transpose_out=True)         # [K_in, T]
     out = fp8mm.fp8_linear_grad_weight(qg, sg, qx, sx)
-    _assert_close(out_f64(out), gemm.linear_grad_weight(rg, rsg, rx, rsx),
+    _assert_close(out_f64(out), gemm.linear_grad_weight(rg, rsg, rx, rsx, out_dtype=None),
                   f"blockwise grad_weight {N_out}x{K_in}x{T}")
 
 
@@ -147,7 +149,7 @@ def _grouped_case(E, N, K, sizes, seed):
     qw, sw, rw, rsw = _quant_both(W.reshape(E * N, K), "rowwise")
     out = fp8mm.fp8_scaled_grouped_mm(qa, qw.reshape(E, N, K), torch.from_numpy(offs).cuda(), sa,
                                       sw.reshape(E, N))
-    ref, written = gemm.grouped_mm(ra, rw.reshape(E, N, K), offs, rsa, rsw.reshape(E, N))
+    ref, written = gemm.grouped_mm(ra, rw.reshape(E, N, K), offs, rsa, rsw.reshape(E, N), out_dtype=None)
     got = out_f64(out)
     assert np.all(got[~written] == 0), "rows no expert owns must not be written"
     return got[written], ref[written]
@@ -170,7 +172,12 @@ def test_grouped_single_expert_equals_rowwise_gemm():
     grouped = fp8mm.fp8_scaled_grouped_mm(qa, qb.reshape(1, 128, 256), torch.tensor([200], dtype=torch.int32,
                                           device="cuda"), sa, sb)
     plain = fp8mm.fp8_scaled_mm(qa, qb, sa, "rowwise", sb, "rowwise")
-    _assert_close(out_f64(grouped), out_f64(plain), "grouped E=1 vs rowwise")
+    ra, rsa = quant.quantize_rowwise(inp["x"])
+    rb, rsb = quant.quantize_rowwise(inp["w"])
+    ref = gemm.scaled_mm(ra, rb, rsa, "rowwise", rsb, "rowwise", out_dtype=None)
+    _assert_close(out_f64(grouped), ref, "grouped E=1")
+    _assert_close(out_f64(plain), ref, "rowwise (same operands)")
+    say(f"grouped E=1 and rowwise outputs bit-identical: {torch.equal(grouped, plain)}")
 
 
 def test_zero_sized_problems():
@@ -209,7 +216,7 @@ def test_full_rowwise_linear_sampled():
     I, J = _sample(x.shape[0], 64, 1), _sample(w.shape[0], 64, 2)
     ra, rsa = quant.quantize_rowwise(x[I])
     rb, rsb = quant.quantize_rowwise(w[J])
-    ref = gemm.scaled_mm(ra, rb, rsa, "rowwise", rsb, "rowwise", bias=quant.bf16_to_f32(bias[J]))
+    ref = gemm.scaled_mm(ra, rb, rsa, "rowwise", rsb, "rowwise", bias=quant.bf16_to_f32(bias[J]), out_dtype=None)
     _assert_close(got[np.ix_(I, J)], ref, "rowwise 8192x4096x4096 sampled")
 
 
@@ -229,7 +236,7 @@ def test_full_blockwise_forward_and_grad_input_sampled(M, N, K):
     for t, s in enumerate(slabs):
         q, sc = quant.quantize_blockwise(w[s * 128:(s + 1) * 128], 128, 128)
         cols = J[t * 16:(t + 1) * 16] - s * 128
-        full = gemm.scaled_mm(rqx, q, rsx, "1x128", sc, "128x128")   # [len(I), 128]
+        full = gemm.scaled_mm(rqx, q, rsx, "1x128", sc, "128x128", out_dtype=None)   # [len(I), 128]
         ref[:, t * 16:(t + 1) * 16] = full[:, cols]
     _assert_close(fwd[np.ix_(I, J)], ref, f"blockwise fwd {M}x{N}x{K} sampled")
     # grad_input = grad_output @ weight, with grad_output [M, N] and weight [N, K]
@@ -239,7 +246,8 @@ def test_full_blockwise_forward_and_grad_input_sampled(M, N, K):
     rqg, rsg = quant.quantize_blockwise(go[I], 1, 128)
     rqw_full, rsw_full = quant.quantize_blockwise(w, 128, 128)
     ref_gi = gemm.scaled_mm_entries(rqg, rqw_full, rsg, "1x128", rsw_full, "128x128",
-                                    np.repeat(np.arange(len(I)), len(Jk)), np.tile(Jk, len(I)), layout="KN")
+                                    np.repeat(np.arange(len(I)), len(Jk)), np.tile(Jk, len(I)), layout="KN",
+                                    out_dtype=None)
     _assert_close(gi[np.ix_(I, Jk)].reshape(-1), ref_gi, f"blockwise grad_input {M}x{K}x{N} sampled")
 
 
@@ -252,7 +260,7 @@ def test_full_blockwise_grad_weight_sampled():
     I, J = _sample(go.shape[1], 48, 7), _sample(x.shape[1], 48, 8)
     rqg, rsg = quant.quantize_blockwise(np.ascontiguousarray(go[:, I]), 128, 1, transpose_out=True)
     rqx, rsx = quant.quantize_blockwise(np.ascontiguousarray(x[:, J]), 128, 1, transpose_out=True)
-    ref = gemm.linear_grad_weight(rqg, rsg, rqx, rsx)
+    ref = gemm.linear_grad_weight(rqg, rsg, rqx, rsx, out_dtype=None)
     _assert_close(gw[np.ix_(I, J)], ref, "blockwise grad_weight 5120x8192x16640 sampled")
 
 
@@ -272,6 +280,6 @@ def test_full_grouped_moe_sampled():
     got, ref = [], []
     for t, (r, e) in enumerate(zip(rows, expert)):
         rw, rsw = quant.quantize_rowwise(W[e][cols])
-        ref.append(gemm.scaled_mm(ra[t:t + 1], rw, rsa[t:t + 1], "rowwise", rsw, "rowwise")[0])
+        ref.append(gemm.scaled_mm(ra[t:t + 1], rw, rsa[t:t + 1], "rowwise", rsw, "rowwise", out_dtype=None)[0])
         got.append(out[r, cols])
     _assert_close(np.array(got), np.array(ref), "grouped E=64 16384x1408x2048 sampled")

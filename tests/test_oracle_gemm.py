@@ -238,3 +238,31 @@ def test_entries_evaluator_matches_full():
     r = rng.integers(0, 64, 500); c = rng.integers(0, 384, 500)
     ent = gemm.scaled_mm_entries(qa, qb, sa, "1x128", sb, "128x128", r, c, layout="KN")
     assert np.array_equal(ent, full[r, c])
+
+
+def test_parity_bars_accept_a_correct_bf16_kernel_and_reject_plausible_bugs():
+    """A result computed exactly, perturbed like fp32 accumulation and rounded
+    once to bf16 meets both bars; a dropped K block, a wrong scale and a
+    transposed operand do not."""
+    g = streams(12, 2)
+    x = normal_bf16(g[0], (256, 1024))
+    w = normal_bf16(g[1], (384, 1024), 0.02)
+    qa, sa = quant.quantize_blockwise(x, 1, 128)
+    qb, sb = quant.quantize_blockwise(w, 128, 128)
+    exact = gemm.scaled_mm_exact(qa, qb, sa, "1x128", sb, "128x128")
+    rng = np.random.default_rng(0)
+    fp32ish = exact * (1 + rng.standard_normal(exact.shape) * 2e-6)
+    good = gemm.round_bf16(fp32ish)
+    rel_f, rel_m = gemm.parity(good, exact)
+    assert rel_f <= 1e-3 and rel_m <= 4e-3
+    # against the once-rounded oracle a single last-place flip can exceed 4e-3
+    flips = (good != gemm.round_bf16(exact))
+    assert flips.any()
+    assert np.max(np.abs(good - gemm.round_bf16(exact)) / np.abs(exact).max()) <= 2.0 ** -7
+    sa_bad = sa.copy(); sa_bad[3] *= 1.01
+    dropped = gemm.scaled_mm(qa, qb, sa, "1x128", sb * np.array([1, 1, 1, 1, 1, 1, 1, 0], np.float32)[None, :], "128x128")
+    wrong_scale = gemm.scaled_mm(qa, qb, sa_bad, "1x128", sb, "128x128")
+    transposed_blk = gemm.scaled_mm(qa, qb, sa, "1x128", np.ascontiguousarray(sb[::-1]), "128x128")
+    for bad in (dropped, wrong_scale, transposed_blk):
+        rel_f, rel_m = gemm.parity(bad, exact)
+        assert rel_f > 1e-3 or rel_m > 4e-3
