@@ -31,6 +31,8 @@
 //  * Grouped (MoE): the tile space is (expert m-tiles) x (N tiles); every
 //    workgroup finds its expert from the device-resident offsets with a
 //    64-lane prefix scan, so no host synchronization is needed.
+#include <type_traits>
+
 #include "launch.hpp"
 
 namespace fp8mm {
@@ -39,7 +41,6 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int BK = 128;
 
@@ -55,7 +56,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Buffer descriptor as four wave-uniform dwords (base, stride 0, size in
+// bytes, gfx9 raw-buffer flags); loads at offsets >= size return zeros.
+typedef int Rsrc __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ Rsrc make_rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return Rsrc{__builtin_amdgcn_readfirstlane(int(uint32_t(a))), __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32))),
+              __builtin_amdgcn_readfirstlane(int(bytes)), 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(__builtin_amdgcn_readfirstlane(
+      int(uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p)))));
+}
+
+// Global -> LDS DMA of 16 (or 4) bytes per lane: lane l writes LDS bytes
+// [lds + 16 l, +16) (or [lds + 4 l, +4)).  Written as inline asm so that the
+// compiler does not attach its own conservative LDS-DMA waits to every LDS
+// read; the kernel tracks these loads itself with s_waitcnt vmcnt.  The
+// instructions have no register results: their operands are consumed at
+// issue.
+__device__ __forceinline__ void dma_b128(Rsrc r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma_b32(Rsrc r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -87,30 +117,57 @@ struct TileInfo {
   const uint16_t* bias;
 };
 
-template <int BM, int BN, int WM, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n) {
-  constexpr int WN = 4 / WM;
-  constexpr int TM = BM / WM;
-  constexpr int TN = BN / WN;
+template <int BM, int BN, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int vec_out) {
+  constexpr int TM = BM / 2;             // 2 x 2 waves
+  constexpr int TN = BN / 2;
   constexpr int FM = TM / 16;
   constexpr int FN = TN / 16;
+  constexpr int STAGES = 3;
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
   constexpr int A_BYTES = BM * BK;
   constexpr int B_BYTES = BN * BK;
-  constexpr int SA_BYTES = BLOCKWISE ? BM * 4 : 0;
-  constexpr int SB_BYTES = EPI == Epi::Block128x1 ? BN * 4 : 0;
+  // Scale regions: every wave owns a 256-byte chunk.  A lane whose DMA
+  // offset is out of range still writes (zeros) to its LDS slot, so each
+  // wave's 64 lanes must land in that wave's own chunk.
+  constexpr int SA_BYTES = BLOCKWISE ? 1024 : 0;     // sA of the tile's BM = 256 rows
+  constexpr int SB_BYTES = BLOCKWISE ? 1024 : 0;     // 128x1: BN = 128 column scales; 128x128: one block scale
   constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "tile shape");
-  static_assert(!BLOCKWISE || TN <= 128, "a wave's columns must sit in one 128-column scale block");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  constexpr int OUTB = OUT_BF16 ? 2 : 4;
+  // epilogue staging: each wave stages TM rows x EPI_COLS outputs at a time
+  // (fp32 output in two column halves), two waves per stage array
+  constexpr int EPI_PASSES = OUT_BF16 ? 1 : 2;
+  constexpr int EPI_COLS = TN / EPI_PASSES;
+  constexpr int EPI_PITCH = EPI_COLS * OUTB + 16;    // padded row pitch
+  static_assert(2 * TM * EPI_PITCH <= STAGE, "epilogue staging must fit in two waves' share of a stage");
+  // direct-to-LDS loads per wave per K step (identical for every wave, so
+  // that one vmcnt immediate tracks the ring)
+  constexpr int LA = BM / 32;
+  constexpr int LB = B_KN ? 0 : BN / 32;
+  constexpr int NCH = BN / 16;                       // KN loader: 16-byte chunks per k row
+  constexpr int KR = B_KN ? BK * NCH / 256 : 1;      // KN loader: k rows per thread
+  constexpr int LKN = B_KN ? KR : 0;
+  constexpr int LS = BLOCKWISE ? 2 : 0;
+  constexpr int LPS = LA + LB + LKN + LS;
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && BM <= 256 && BN <= 256, "tile shape");
+  static_assert(!BLOCKWISE || (BM == 256 && BN == 128), "blockwise tiles are 256 x 128");
+  static_assert(!B_KN || KR == 4 || KR == 8, "KN loader shape");
+  static_assert(STAGES * STAGE <= 160 * 1024, "LDS budget");
+  // One LDS array per stage: with the stage index a compile-time constant the
+  // compiler can tell the DMA writes into the prefetch stage from the reads
+  // of the current one and does not drain the whole ring at every step.
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[STAGE];
+  auto stage_ptr = [&](int s) -> uint8_t* { return s == 0 ? stage0 : (s == 1 ? stage1 : stage2); };
+  // the output staging of the epilogue uses stage0 (waves 0, 1) and stage1 (waves 2, 3)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---------------- tile selection ----------------
-  const int nblk = gridDim.x;
-  const int per_xcd = nblk / 8;   // the launcher pads the grid to a multiple of 8
+  const int per_xcd = gridDim.x / 8;   // the launcher pads the grid to a multiple of 8
   const int lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   TileInfo ti;
   if constexpr (!GROUPED) {
@@ -179,73 +236,79 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m
   const int nk = (K + BK - 1) / BK;
 
   // ---------------- loaders ----------------
-  // Direct-to-LDS loads: instruction i of wave w fills tile rows
-  // [(i*4 + w) * 8, +8); lane l writes LDS bytes [16 l, 16 l + 16) of that
+  // Direct-to-LDS: load number q < LA of wave w fills tile rows
+  // [(q*4 + w) * 8, +8); lane l writes LDS bytes [16 l, 16 l + 16) of that
   // 1 KiB span, i.e. row l/8, slot l%8, which holds chunk (l%8) ^ (l/8).
   const int ld_row = lane >> 3;
   const int ld_chunk = (lane & 7) ^ ld_row;
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(ti.A, uint32_t(ti.rows_valid) * uint32_t(p.lda));
-  __amdgpu_buffer_rsrc_t rsB;
-  if constexpr (!B_KN) rsB = make_rsrc(ti.B, uint32_t(ti.cols_valid) * uint32_t(p.ldb));
+  const Rsrc rsA = make_rsrc4(ti.A, uint32_t(ti.rows_valid) * uint32_t(p.lda));
+  __amdgpu_buffer_rsrc_t rsB;             // B stored [K, N]: register loads
+  Rsrc rsB4;                              // B stored [N, K]: DMA
+  if constexpr (!B_KN) rsB4 = make_rsrc4(ti.B, uint32_t(ti.cols_valid) * uint32_t(p.ldb));
   else rsB = make_rsrc(ti.B, uint32_t(K) * uint32_t(p.ldb) - uint32_t(ti.n0));
 
-  auto issue_direct = [&](int stage, int kt) {
-    uint8_t* st = smem + stage * STAGE;
+  // Issue load number q (0 <= q < LA + LB + LS) of K step kt into its stage.
+  // Past the last K step the same instructions are issued with out-of-range
+  // offsets: they return zeros into a stage nobody reads, keep the per-step
+  // load count uniform for the vmcnt bookkeeping and need no branches.
+  auto issue_one = [&](int q, int stage, int kt, bool live) {
+    uint8_t* st = stage_ptr(stage);
     const int k0 = kt * BK;
-    const bool kin = k0 + ld_chunk * 16 < K;
-#pragma unroll
-    for (int i = 0; i < BM / 32; ++i) {
-      const int r = (i * 4 + wave) * 8 + ld_row;
+    const bool kin = live && (k0 + ld_chunk * 16 < K);
+    if (q < LA) {
+      const int r = (q * 4 + wave) * 8 + ld_row;
       const uint32_t off = kin ? uint32_t(r) * uint32_t(p.lda) + uint32_t(k0 + ld_chunk * 16) : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr)(st + (i * 4 + wave) * 1024), 16, off, 0, 0, 0);
-    }
-    if constexpr (!B_KN) {
-#pragma unroll
-      for (int i = 0; i < BN / 32; ++i) {
-        const int r = (i * 4 + wave) * 8 + ld_row;
-        const uint32_t off = kin ? uint32_t(r) * uint32_t(p.ldb) + uint32_t(k0 + ld_chunk * 16) : 0x80000000u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr)(st + A_BYTES + (i * 4 + wave) * 1024), 16, off,
-                                                 0, 0, 0);
-      }
-    }
-    if constexpr (BLOCKWISE) {
-      // sA[kb, row0 .. row0 + BM) -> LDS, one float per lane (scale rows are
-      // only 4-byte aligned).  The descriptor spans to the end of the scale
-      // array, so no load is partly out of range; rows past the tile edge
-      // read neighbouring scales that only reach rows which are never stored.
-      if (wave * 64 < BM) {
+      dma_b128(rsA, lds_addr(st + (q * 4 + wave) * 1024), off);
+    } else if (q < LA + LB) {
+      const int qb = q - LA;
+      const int r = (qb * 4 + wave) * 8 + ld_row;
+      const uint32_t off = kin ? uint32_t(r) * uint32_t(p.ldb) + uint32_t(k0 + ld_chunk * 16) : 0x80000000u;
+      dma_b128(rsB4, lds_addr(st + A_BYTES + (qb * 4 + wave) * 1024), off);
+    } else if (q == LA + LB) {
+      if constexpr (BLOCKWISE) {
+        // sA[kb, row0 .. row0 + BM): BM/4 floats per wave, one per lane.  The
+        // descriptor spans to the end of the scale array, so no load is partly
+        // out of range; rows past the tile edge read neighbouring scales that
+        // only reach rows which are never stored.
         const int64_t off = int64_t(kt) * p.M + ti.row0 + wave * 64;
         const int64_t rem = int64_t(nk) * p.M - off;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.sa + (rem > 0 ? off : 0), uint32_t(rem > 0 ? rem * 4 : 0));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(st + A_BYTES + B_BYTES + wave * 256), 4,
-                                                 uint32_t(lane) * 4u, 0, 0, 0);
+        const Rsrc rs = make_rsrc4(p.sa + (rem > 0 ? off : 0), uint32_t(rem > 0 ? rem * 4 : 0));
+        const uint32_t voff = live ? uint32_t(lane) * 4u : 0x80000000u;
+        dma_b32(rs, lds_addr(st + A_BYTES + B_BYTES + wave * 256), voff);
       }
+    } else {
       if constexpr (EPI == Epi::Block128x1) {
-        if (wave * 64 < BN) {
-          const int64_t off = int64_t(kt) * p.N + ti.n0 + wave * 64;
-          const int64_t rem = int64_t(nk) * p.N - off;
-          const __amdgpu_buffer_rsrc_t rs = make_rsrc(ti.sb + (rem > 0 ? off : 0), uint32_t(rem > 0 ? rem * 4 : 0));
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(st + A_BYTES + B_BYTES + SA_BYTES + wave * 256),
-                                                   4, uint32_t(lane) * 4u, 0, 0, 0);
-        }
+        // waves 0 and 1 fetch the 128 column scales; waves 2 and 3 write zeros
+        // into their own (unused) chunks
+        const int64_t off = int64_t(kt) * p.N + ti.n0 + (wave & 1) * 64;
+        const int64_t rem = int64_t(nk) * p.N - off;
+        const Rsrc rs = make_rsrc4(ti.sb + (rem > 0 ? off : 0), uint32_t(rem > 0 ? rem * 4 : 0));
+        const uint32_t voff = (live && wave < 2) ? uint32_t(lane) * 4u : 0x80000000u;
+        dma_b32(rs, lds_addr(st + A_BYTES + B_BYTES + SA_BYTES + wave * 256), voff);
+      } else if constexpr (EPI == Epi::Block128x128) {
+        // the weight-block scale of (n-block, kb): one float, fetched by lane 0 of wave 0
+        const int64_t nb = ti.n0 / 128;
+        const int64_t idx = B_KN ? int64_t(kt) * (p.N / 128) + nb : nb * nk + kt;
+        const int64_t total = int64_t(nk) * (p.N / 128);
+        const Rsrc rs = make_rsrc4(ti.sb, uint32_t(total * 4));
+        const uint32_t voff = (live && wave == 0 && lane == 0) ? uint32_t(idx) * 4u : 0x80000000u;
+        dma_b32(rs, lds_addr(st + A_BYTES + B_BYTES + SA_BYTES + wave * 256), voff);
       }
     }
   };
+  constexpr int LDIRECT = LA + LB + LS;
 
   // B stored [K, N]: thread t loads KR consecutive k rows x 16 n bytes and
-  // writes them transposed (n rows of the [N][128] tile).
-  constexpr int NCH = BN / 16;              // 16-byte chunks per k row
-  constexpr int KR = BK * NCH / 256;       // k rows per thread
-  static_assert(!B_KN || KR == 4 || KR == 8, "KN loader shape");
+  // writes them transposed into the [N][128] tile (v_perm_b32 4x4 transposes).
   const int kn_nc = tid % NCH;
   const int kn_kg = tid / NCH;
-  v4i kn_regs[B_KN ? KR : 1];
-  auto kn_load = [&](int kt) {
+  v4i kn_regs[KR];
+  auto kn_load = [&](int kt, bool live) {
     if constexpr (B_KN) {
       const int k0 = kt * BK + kn_kg * KR;
 #pragma unroll
       for (int r = 0; r < KR; ++r) {
-        const bool in = (k0 + r < K) && (kn_nc * 16 < ti.cols_valid);
+        const bool in = live && (k0 + r < K) && (kn_nc * 16 < ti.cols_valid);
         const uint32_t off = in ? uint32_t(k0 + r) * uint32_t(p.ldb) + uint32_t(kn_nc * 16) : 0x80000000u;
         kn_regs[r] = __builtin_amdgcn_raw_buffer_load_b128(rsB, off, 0, 0);
       }
@@ -253,9 +316,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m
   };
   auto kn_store = [&](int stage) {
     if constexpr (B_KN) {
-      uint8_t* bt = smem + stage * STAGE + A_BYTES;
+      uint8_t* bt = stage_ptr(stage) + A_BYTES;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {          // 4-byte column group within the 16-byte chunk
+      for (int q = 0; q < 4; ++q) {
         uint32_t cols[KR / 4][4];
 #pragma unroll
         for (int h = 0; h < KR / 4; ++h) {
@@ -266,21 +329,20 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m
 #pragma unroll
         for (int jn = 0; jn < 4; ++jn) {
           const int n = kn_nc * 16 + q * 4 + jn;
-          const int kl = kn_kg * KR;            // first k byte within the 128-byte row
+          const int kl = kn_kg * KR;
           uint8_t* dst = bt + lds_off(n, kl >> 4) + (kl & 15);
-          if constexpr (KR == 8) {
+          if constexpr (KR == 8)
             *reinterpret_cast<uint2*>(dst) = make_uint2(cols[0][jn], cols[1][jn]);
-          } else {
+          else
             *reinterpret_cast<uint32_t*>(dst) = cols[0][jn];
-          }
         }
       }
     }
   };
 
   // ---------------- accumulators ----------------
-  const int wm = wave % WM;
-  const int wn = wave / WM;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
   const int row_base = wm * TM;
   const int col_base = wn * TN;
   const int frow = lane & 15;   // fragment row (A) / column (B) of this lane
@@ -291,115 +353,196 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int stage, int kt) {
-    const uint8_t* As = smem + stage * STAGE;
+  auto read_frag = [&](const uint8_t* tile, int r) {
+    const v4i lo = *reinterpret_cast<const v4i*>(tile + lds_off(r, 2 * fq));
+    const v4i hi = *reinterpret_cast<const v4i*>(tile + lds_off(r, 2 * fq + 1));
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+
+  // One K step on stage (kt % STAGES).  The direct loads of K step kt + 2
+  // (zeros past the end) are spread over the fragment rows, the A fragment of
+  // the next row is read one row ahead, and sched_barrier fences pin the
+  // order (MFMA q, promotion of MFMA q-1) so that every MFMA overlaps the
+  // VALU work of its predecessor instead of waiting for it.
+  auto compute = [&](auto stage_c, int kt, bool live_next) {
+    constexpr int S = decltype(stage_c)::value;
+    const uint8_t* As = stage_ptr(S);
     const uint8_t* Bs = As + A_BYTES;
+    [[maybe_unused]] const float* sas = reinterpret_cast<const float*>(As + A_BYTES + B_BYTES);
+    [[maybe_unused]] const float* sbs = reinterpret_cast<const float*>(As + A_BYTES + B_BYTES + SA_BYTES);
+    v8i a_cur = read_frag(As, row_base + frow);
     v8i b[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r = col_base + j * 16 + frow;
-      const v4i lo = *reinterpret_cast<const v4i*>(Bs + lds_off(r, 2 * fq));
-      const v4i hi = *reinterpret_cast<const v4i*>(Bs + lds_off(r, 2 * fq + 1));
-      b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
+    for (int j = 0; j < FN; ++j) b[j] = read_frag(Bs, col_base + j * 16 + frow);
     [[maybe_unused]] float sbk = 0.f;
     [[maybe_unused]] float sbv[FN];
-    if constexpr (EPI == Epi::Block128x128) {
-      const int64_t nb = (ti.n0 + col_base) / 128;
-      sbk = B_KN ? ti.sb[int64_t(kt) * (p.N / 128) + nb] : ti.sb[nb * (K / BK) + kt];
-    }
-    if constexpr (EPI == Epi::Block128x1) {
-      const float* sbs = reinterpret_cast<const float*>(As + A_BYTES + B_BYTES + SA_BYTES);
+    [[maybe_unused]] v4f fa_cur;
+    if constexpr (BLOCKWISE) {
+      fa_cur = *reinterpret_cast<const v4f*>(sas + row_base + fq * 4);
+      if constexpr (EPI == Epi::Block128x128) sbk = sbs[0];
+      if constexpr (EPI == Epi::Block128x1) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sbv[j] = sbs[col_base + j * 16 + frow];
+        for (int j = 0; j < FN; ++j) sbv[j] = sbs[col_base + j * 16 + frow];
+      }
     }
+    [[maybe_unused]] v4f t_prev = v4f{0.f, 0.f, 0.f, 0.f};
+    [[maybe_unused]] v4f f_prev = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int r = row_base + i * 16 + frow;
-      const v4i lo = *reinterpret_cast<const v4i*>(As + lds_off(r, 2 * fq));
-      const v4i hi = *reinterpret_cast<const v4i*>(As + lds_off(r, 2 * fq + 1));
-      const v8i a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int q = i * LDIRECT / FM; q < (i + 1) * LDIRECT / FM; ++q) issue_one(q, (S + 2) % STAGES, kt + 2, live_next);
+      v8i a_next = a_cur;
+      [[maybe_unused]] v4f fa_next;
+      if (i + 1 < FM) {
+        a_next = read_frag(As, row_base + (i + 1) * 16 + frow);
+        if constexpr (BLOCKWISE) fa_next = *reinterpret_cast<const v4f*>(sas + row_base + (i + 1) * 16 + fq * 4);
+      }
       if constexpr (!BLOCKWISE) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_16x16x128(a, b[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) {
+          acc[i][j] = mfma_16x16x128(a_cur, b[j], acc[i][j]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       } else {
-        const float* sas = reinterpret_cast<const float*>(As + A_BYTES + B_BYTES);
-        v4f fa = *reinterpret_cast<const v4f*>(sas + row_base + i * 16 + fq * 4);
+        v4f fa = fa_cur;
         if constexpr (EPI == Epi::Block128x128) fa = fa * sbk;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const v4f t = mfma_16x16x128(a, b[j], v4f{0.f, 0.f, 0.f, 0.f});
-          if constexpr (EPI == Epi::Block128x128) {
+          const v4f t = mfma_16x16x128(a_cur, b[j], v4f{0.f, 0.f, 0.f, 0.f});
+          if (i > 0 || j > 0) {
+            const int ip = j > 0 ? i : i - 1;
+            const int jp = j > 0 ? j - 1 : FN - 1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(t[e], fa[e], acc[i][j][e]);
+            for (int e = 0; e < 4; ++e) acc[ip][jp][e] = __builtin_fmaf(t_prev[e], f_prev[e], acc[ip][jp][e]);
+          }
+          t_prev = t;
+          if constexpr (EPI == Epi::Block128x128) {
+            f_prev = fa;
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(t[e] * sbv[j], fa[e], acc[i][j][e]);
+            for (int e = 0; e < 4; ++e) f_prev[e] = fa[e] * sbv[j];
           }
+          // within this region: the MFMA issues first, the VALU work after it
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        fa_cur = fa_next;
       }
+      a_cur = a_next;
+    }
+    if constexpr (BLOCKWISE) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[FM - 1][FN - 1][e] = __builtin_fmaf(t_prev[e], f_prev[e], acc[FM - 1][FN - 1][e]);
     }
   };
 
-  // ---------------- main loop ----------------
+  // ---------------- main loop: 3-stage ring, prefetch distance 2 ----------------
+  auto step = [&](auto stage_c, int kt) {
+    constexpr int S = decltype(stage_c)::value;
+    // Stage kt is complete once only the newest step's loads are in flight.
+    // A bare s_barrier (not __syncthreads, whose release fence would drain
+    // every outstanding load): each wave first retires its own DMA for this
+    // stage and its LDS reads / writes, so after the barrier the stage is
+    // complete and the stage refilled next is no longer being read.
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS) : "memory");
+    const bool live = kt + 2 < nk;
+    kn_load(kt + 2, live);
+    compute(stage_c, kt, live);
+    kn_store((S + 2) % STAGES);
+  };
   if (nk > 0) {
-    issue_direct(0, 0);
-    kn_load(0);
+#pragma unroll
+    for (int q = 0; q < LDIRECT; ++q) issue_one(q, 0, 0, true);
+    kn_load(0, true);
     kn_store(0);
-    wait_vmem();
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int s = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        issue_direct(s ^ 1, kt + 1);
-        kn_load(kt + 1);
-      }
-      compute(s, kt);
-      if (more) kn_store(s ^ 1);
-      wait_vmem();
-      __syncthreads();
+#pragma unroll
+    for (int q = 0; q < LDIRECT; ++q) issue_one(q, 1, 1, nk > 1);
+    kn_load(1, nk > 1);
+    kn_store(1);
+    for (int kt = 0; kt < nk; kt += 3) {
+      step(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+      if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
     }
   }
 
-  // ---------------- epilogue ----------------
+  // ---------------- epilogue: scale, round, stage in LDS, 16-byte stores ----------------
+  // Every DMA of the ring (including the zero loads issued past the last K
+  // step into spare stages) has landed before the stages are reused below.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();   // every wave is done with the ring
+  uint8_t* ep = (wave < 2 ? stage0 : stage1) + (wave & 1) * TM * EPI_PITCH;
   [[maybe_unused]] float s_tensor = 0.f;
   if constexpr (EPI == Epi::Tensor) s_tensor = p.sa[0] * p.sb[0];
+  [[maybe_unused]] float sar[FM][4];
+  if constexpr (EPI == Epi::Row) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int rl = row_base + i * 16 + fq * 4;   // local row of element 0
-    [[maybe_unused]] float sar[4];
-    if constexpr (EPI == Epi::Row) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sar[e] = (rl + e < ti.rows_valid) ? p.sa[ti.row0 + rl + e] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int cl = col_base + j * 16 + frow;
-      if (cl >= ti.cols_valid) continue;
-      const int64_t col = ti.n0 + cl;
-      [[maybe_unused]] float sbc = 0.f;
-      if constexpr (EPI == Epi::Row) sbc = ti.sb[col];
-      float bias_v = 0.f;
-      if constexpr (BIAS) bias_v = __uint_as_float(uint32_t(ti.bias[col]) << 16);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (rl + e >= ti.rows_valid) continue;
-        float v = acc[i][j][e];
-        if constexpr (EPI == Epi::Tensor) v = v * s_tensor;
-        if constexpr (EPI == Epi::Row) v = (v * sar[e]) * sbc;
-        if constexpr (BIAS) v = v + bias_v;
-        const int64_t row = ti.row0 + rl + e;
-        if constexpr (OUT_BF16)
-          reinterpret_cast<uint16_t*>(p.out)[row * p.ldo + col] = f32_to_bf16_rne(v);
-        else
-          reinterpret_cast<float*>(p.out)[row * p.ldo + col] = v;
+        const int rt = row_base + i * 16 + fq * 4 + e;   // row within the block tile
+        sar[i][e] = rt < ti.rows_valid ? p.sa[ti.row0 + rt] : 0.f;
+      }
+  }
+#pragma unroll
+  for (int pass = 0; pass < EPI_PASSES; ++pass) {
+    constexpr int FNP = FN / EPI_PASSES;
+#pragma unroll
+    for (int jj = 0; jj < FNP; ++jj) {
+      const int j = pass * FNP + jj;
+      const int cl = jj * 16 + frow;                  // column within this pass
+      const int ct = col_base + j * 16 + frow;        // column within the block tile
+      const bool cin = ct < ti.cols_valid;
+      [[maybe_unused]] float sbc = 0.f;
+      if constexpr (EPI == Epi::Row) sbc = cin ? ti.sb[ti.n0 + ct] : 0.f;
+      float bias_v = 0.f;
+      if constexpr (BIAS) bias_v = cin ? __uint_as_float(uint32_t(ti.bias[ti.n0 + ct]) << 16) : 0.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = acc[i][j][e];
+          if constexpr (EPI == Epi::Tensor) v = v * s_tensor;
+          if constexpr (EPI == Epi::Row) v = (v * sar[i][e]) * sbc;
+          if constexpr (BIAS) v = v + bias_v;
+          uint8_t* dst = ep + (i * 16 + fq * 4 + e) * EPI_PITCH + cl * OUTB;
+          if constexpr (OUT_BF16)
+            *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_rne(v);
+          else
+            *reinterpret_cast<float*>(dst) = v;
+        }
       }
     }
+    __syncthreads();
+    constexpr int CPR = EPI_COLS * OUTB / 16;       // 16-byte chunks per staged row
+    constexpr int EPR = 16 / OUTB;                  // elements per chunk
+#pragma unroll 4
+    for (int idx = lane; idx < TM * CPR; idx += 64) {
+      const int rl = idx / CPR;
+      const int ch = idx % CPR;
+      const int rt = row_base + rl;
+      const int ct = col_base + pass * EPI_COLS + ch * EPR;
+      if (rt >= ti.rows_valid || ct >= ti.cols_valid) continue;
+      const uint8_t* src = ep + rl * EPI_PITCH + ch * 16;
+      uint8_t* dst = reinterpret_cast<uint8_t*>(p.out) + ((ti.row0 + rt) * p.ldo + ti.n0 + ct) * OUTB;
+      if (vec_out && ct + EPR <= ti.cols_valid) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        const int n = min(EPR, ti.cols_valid - ct);
+        for (int e = 0; e < n; ++e) {
+          if constexpr (OUT_BF16)
+            reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+          else
+            reinterpret_cast<float*>(dst)[e] = reinterpret_cast<const float*>(src)[e];
+        }
+      }
+    }
+    if (pass + 1 < EPI_PASSES) __syncthreads();
   }
 }
 
-template <int BM, int BN, int WM, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED>
+template <int BM, int BN, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
   int tiles_m, tiles_n = int((p.N + BN - 1) / BN);
   if (GROUPED)
@@ -409,19 +552,19 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
   const int64_t tiles = int64_t(tiles_m) * tiles_n;
   if (tiles == 0) return hipSuccess;
   const int grid = int((tiles + 7) / 8 * 8);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, EPI, B_KN, OUT_BF16, BIAS, GROUPED>), dim3(grid), dim3(256), 0, st, p,
-                     tiles_m, tiles_n);
+  const int outb = p.out_bf16 ? 2 : 4;
+  const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, B_KN, OUT_BF16, BIAS, GROUPED>), dim3(grid), dim3(256), 0, st, p,
+                     tiles_m, tiles_n, vec_out);
   return hipGetLastError();
 }
 
 template <Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED>
 hipError_t launch_epi(const GemmProblem& p, hipStream_t st) {
   if constexpr (GROUPED)
-    return launch_cfg<128, 128, 2, EPI, false, OUT_BF16, BIAS, true>(p, st);
-  else if constexpr (EPI == Epi::Block128x128 || EPI == Epi::Block128x1)
-    return launch_cfg<256, 128, 2, EPI, B_KN, OUT_BF16, BIAS, false>(p, st);
+    return launch_cfg<128, 128, EPI, false, OUT_BF16, BIAS, true>(p, st);
   else
-    return launch_cfg<256, 256, 2, EPI, B_KN, OUT_BF16, BIAS, false>(p, st);
+    return launch_cfg<256, 128, EPI, B_KN, OUT_BF16, BIAS, false>(p, st);
 }
 
 template <Epi EPI, bool B_KN, bool GROUPED>
