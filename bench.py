@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-recipes", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (optional)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device-to-device copy (3 times), so that a rocprofv3 "
+                         "counter run sees FETCH_SIZE / WRITE_SIZE of a kernel with known traffic")
     return ap.parse_args()
 
 
@@ -234,6 +237,15 @@ def main():
     W = build_workloads(torch, fp8mm, workloads)
     if args.workload not in W:
         raise SystemExit(f"unknown workload {args.workload}; choose from {sorted(W)}")
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] calibration copy: 3 x 512 MiB device-to-device", file=sys.stderr, flush=True)
 
     print(f"[bench] building inputs for {args.workload}", file=sys.stderr, flush=True)
     wl = W[args.workload]()

@@ -50,7 +50,13 @@ __device__ __forceinline__ v4f mfma_16x16x128(const v8i& a, const v8i& b, const 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// LDS tile rows are 128 bytes; 16-byte chunk c of row r is stored at slot
+// c ^ ((r >> 1) & 7).  A 16x16 fragment read has 16 lanes of 16 bytes in
+// flight per LDS cycle, one per row of a 16-row group: the swizzle gives the
+// 16 rows distinct (row parity, slot) pairs, i.e. distinct bank groups of the
+// 64-bank LDS.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -77,15 +83,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // read; the kernel tracks these loads itself with s_waitcnt vmcnt.  The
 // instructions have no register results: their operands are consumed at
 // issue.
-__device__ __forceinline__ void dma_b128(Rsrc r, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+__device__ __forceinline__ void dma_b128(Rsrc r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  soff = uint32_t(__builtin_amdgcn_readfirstlane(int(soff)));
+  lds = uint32_t(__builtin_amdgcn_readfirstlane(int(lds)));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(r),
+               "s"(soff)
                : "memory", "m0");
 }
 
 __device__ __forceinline__ void dma_b32(Rsrc r, uint32_t lds, uint32_t voff) {
+  lds = uint32_t(__builtin_amdgcn_readfirstlane(int(lds)));
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
                : "memory", "m0");
 }
+
+// The same descriptor with no valid bytes: every lane's load returns zero.
+__device__ __forceinline__ Rsrc dead(Rsrc r) { return Rsrc{r.x, r.y, 0, r.w}; }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -117,50 +130,61 @@ struct TileInfo {
   const uint16_t* bias;
 };
 
-template <int BM, int BN, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int vec_out) {
-  constexpr int TM = BM / 2;             // 2 x 2 waves
-  constexpr int TN = BN / 2;
+constexpr int epi_passes(int nw, int tm, int tn, int outb, int stage) {
+  // smallest number of column passes whose staging (nw/2 waves per stage
+  // array, TM rows each, padded pitch) fits in one stage array
+  for (int pz = 1; pz <= 4; pz *= 2)
+    if ((nw / 2) * tm * ((tn / pz) * outb + 16) <= stage) return pz;
+  return 8;
+}
+
+template <int BM, int BN, int NW, int STAGES, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED, bool K_ALIGNED>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int vec_out) {
+  constexpr int NT = NW * 64;
+  constexpr int WN = NW / 2;             // waves: 2 along M x NW/2 along N
+  constexpr int TM = BM / 2;
+  constexpr int TN = BN / WN;
   constexpr int FM = TM / 16;
   constexpr int FN = TN / 16;
-  constexpr int STAGES = 3;
+  constexpr int D = STAGES - 1;          // prefetch distance in K steps
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
   constexpr int A_BYTES = BM * BK;
   constexpr int B_BYTES = BN * BK;
-  // Scale regions: every wave owns a 256-byte chunk.  A lane whose DMA
-  // offset is out of range still writes (zeros) to its LDS slot, so each
-  // wave's 64 lanes must land in that wave's own chunk.
-  constexpr int SA_BYTES = BLOCKWISE ? 1024 : 0;     // sA of the tile's BM = 256 rows
-  constexpr int SB_BYTES = BLOCKWISE ? 1024 : 0;     // 128x1: BN = 128 column scales; 128x128: one block scale
+  // Scale regions (blockwise): 8 chunks of 256 bytes, 4 for sA (BM = 256
+  // rows) and 4 for sB (128x1: up to 256 column scales; 128x128: one block
+  // scale per 128 columns, at the start of its chunk).  Each chunk is filled
+  // by one wave's 64 lanes: a lane whose DMA offset is out of range still
+  // writes (zeros) to its LDS slot, so a wave must own its whole chunk.
+  constexpr int SA_BYTES = BLOCKWISE ? 1024 : 0;
+  constexpr int SB_BYTES = BLOCKWISE ? 1024 : 0;
   constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
   constexpr int OUTB = OUT_BF16 ? 2 : 4;
-  // epilogue staging: each wave stages TM rows x EPI_COLS outputs at a time
-  // (fp32 output in two column halves), two waves per stage array
-  constexpr int EPI_PASSES = OUT_BF16 ? 1 : 2;
+  constexpr int EPI_PASSES = epi_passes(NW, TM, TN, OUTB, STAGE);
   constexpr int EPI_COLS = TN / EPI_PASSES;
   constexpr int EPI_PITCH = EPI_COLS * OUTB + 16;    // padded row pitch
-  static_assert(2 * TM * EPI_PITCH <= STAGE, "epilogue staging must fit in two waves' share of a stage");
-  // direct-to-LDS loads per wave per K step (identical for every wave, so
-  // that one vmcnt immediate tracks the ring)
-  constexpr int LA = BM / 32;
-  constexpr int LB = B_KN ? 0 : BN / 32;
+  // loads per wave per K step (identical for every wave, so that one vmcnt
+  // immediate tracks the ring)
+  constexpr int LA = BM / (8 * NW);
+  constexpr int LB = B_KN ? 0 : BN / (8 * NW);
   constexpr int NCH = BN / 16;                       // KN loader: 16-byte chunks per k row
-  constexpr int KR = B_KN ? BK * NCH / 256 : 1;      // KN loader: k rows per thread
+  constexpr int KR = B_KN ? BK * NCH / NT : 1;       // KN loader: k rows per thread
   constexpr int LKN = B_KN ? KR : 0;
-  constexpr int LS = BLOCKWISE ? 2 : 0;
+  constexpr int LS = BLOCKWISE ? 8 / NW : 0;
   constexpr int LPS = LA + LB + LKN + LS;
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && BM <= 256 && BN <= 256, "tile shape");
-  static_assert(!BLOCKWISE || (BM == 256 && BN == 128), "blockwise tiles are 256 x 128");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(STAGES == 2 || STAGES == 3, "2 or 3 stages");
+  static_assert(TM % 16 == 0 && TN % 16 == 0 && LA >= 1 && (B_KN || LB >= 1), "tile shape");
+  static_assert(!BLOCKWISE || (BM == 256 && BN % 128 == 0 && 128 % TN == 0), "blockwise tile shape");
   static_assert(!B_KN || KR == 4 || KR == 8, "KN loader shape");
   static_assert(STAGES * STAGE <= 160 * 1024, "LDS budget");
-  // One LDS array per stage: with the stage index a compile-time constant the
-  // compiler can tell the DMA writes into the prefetch stage from the reads
-  // of the current one and does not drain the whole ring at every step.
+  static_assert(EPI_PASSES <= 4 && TN % EPI_PASSES == 0, "epilogue staging");
+  // One LDS array per stage: with every stage index a compile-time constant,
+  // reads of the current stage and DMA into the prefetch stage are visibly
+  // distinct.
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[STAGES > 2 ? STAGE : 16];
   auto stage_ptr = [&](int s) -> uint8_t* { return s == 0 ? stage0 : (s == 1 ? stage1 : stage2); };
-  // the output staging of the epilogue uses stage0 (waves 0, 1) and stage1 (waves 2, 3)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -237,62 +261,75 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m
 
   // ---------------- loaders ----------------
   // Direct-to-LDS: load number q < LA of wave w fills tile rows
-  // [(q*4 + w) * 8, +8); lane l writes LDS bytes [16 l, 16 l + 16) of that
-  // 1 KiB span, i.e. row l/8, slot l%8, which holds chunk (l%8) ^ (l/8).
+  // [(q*NW + w) * 8, +8); lane l writes LDS bytes [16 l, 16 l + 16) of that
+  // 1 KiB span, i.e. row l/8 of the span, slot l%8, which holds chunk
+  // (l%8) ^ swz(row).  The span starts at a multiple of 8 rows and NW is
+  // even, so swz(row) = ((w & 1) << 2) | (l >> 4) for every q.
   const int ld_row = lane >> 3;
-  const int ld_chunk = (lane & 7) ^ ld_row;
+  const int ld_chunk = (lane & 7) ^ (((wave & 1) << 2) | (lane >> 4));
   const Rsrc rsA = make_rsrc4(ti.A, uint32_t(ti.rows_valid) * uint32_t(p.lda));
   __amdgpu_buffer_rsrc_t rsB;             // B stored [K, N]: register loads
   Rsrc rsB4;                              // B stored [N, K]: DMA
   if constexpr (!B_KN) rsB4 = make_rsrc4(ti.B, uint32_t(ti.cols_valid) * uint32_t(p.ldb));
   else rsB = make_rsrc(ti.B, uint32_t(K) * uint32_t(p.ldb) - uint32_t(ti.n0));
+  // per-lane byte offsets of each load at k = 0; the K position is the
+  // instruction's scalar offset
+  uint32_t voffA[LA];
+#pragma unroll
+  for (int q = 0; q < LA; ++q) voffA[q] = uint32_t((q * NW + wave) * 8 + ld_row) * uint32_t(p.lda) + ld_chunk * 16;
+  uint32_t voffB[LB > 0 ? LB : 1];
+#pragma unroll
+  for (int q = 0; q < LB; ++q) voffB[q] = uint32_t((q * NW + wave) * 8 + ld_row) * uint32_t(p.ldb) + ld_chunk * 16;
+  const uint32_t lds0 = lds_addr(stage0), lds1 = lds_addr(stage1), lds2 = lds_addr(stage2);
+  auto stage_lds = [&](int s) -> uint32_t { return s == 0 ? lds0 : (s == 1 ? lds1 : lds2); };
+  constexpr bool k_ragged = !K_ALIGNED;   // K % 128 != 0 is possible
 
   // Issue load number q (0 <= q < LA + LB + LS) of K step kt into its stage.
-  // Past the last K step the same instructions are issued with out-of-range
-  // offsets: they return zeros into a stage nobody reads, keep the per-step
-  // load count uniform for the vmcnt bookkeeping and need no branches.
+  // Past the last K step the same instructions go through a descriptor with
+  // no valid bytes: they write zeros into a stage nobody reads and keep the
+  // per-step load count uniform for the vmcnt bookkeeping, without branches.
   auto issue_one = [&](int q, int stage, int kt, bool live) {
-    uint8_t* st = stage_ptr(stage);
-    const int k0 = kt * BK;
-    const bool kin = live && (k0 + ld_chunk * 16 < K);
+    const uint32_t st = stage_lds(stage);
+    const uint32_t k0 = uint32_t(kt) * BK;
+    const bool tail = k_ragged && (int(k0) + BK > K);   // K_ALIGNED: folds to false
     if (q < LA) {
-      const int r = (q * 4 + wave) * 8 + ld_row;
-      const uint32_t off = kin ? uint32_t(r) * uint32_t(p.lda) + uint32_t(k0 + ld_chunk * 16) : 0x80000000u;
-      dma_b128(rsA, lds_addr(st + (q * 4 + wave) * 1024), off);
+      const Rsrc r = live ? rsA : dead(rsA);
+      uint32_t vo = voffA[q];
+      if (tail) vo = (int(k0) + ld_chunk * 16 < K) ? vo : 0x80000000u;
+      dma_b128(r, st + (q * NW + wave) * 1024, vo, k0);
     } else if (q < LA + LB) {
       const int qb = q - LA;
-      const int r = (qb * 4 + wave) * 8 + ld_row;
-      const uint32_t off = kin ? uint32_t(r) * uint32_t(p.ldb) + uint32_t(k0 + ld_chunk * 16) : 0x80000000u;
-      dma_b128(rsB4, lds_addr(st + A_BYTES + (qb * 4 + wave) * 1024), off);
-    } else if (q == LA + LB) {
-      if constexpr (BLOCKWISE) {
-        // sA[kb, row0 .. row0 + BM): BM/4 floats per wave, one per lane.  The
-        // descriptor spans to the end of the scale array, so no load is partly
-        // out of range; rows past the tile edge read neighbouring scales that
-        // only reach rows which are never stored.
-        const int64_t off = int64_t(kt) * p.M + ti.row0 + wave * 64;
+      const Rsrc r = live ? rsB4 : dead(rsB4);
+      uint32_t vo = voffB[qb];
+      if (tail) vo = (int(k0) + ld_chunk * 16 < K) ? vo : 0x80000000u;
+      dma_b128(r, st + A_BYTES + (qb * NW + wave) * 1024, vo, k0);
+    } else if constexpr (BLOCKWISE) {
+      const int c = (q - LA - LB) * NW + wave;        // scale chunk 0..7 of this wave
+      if (c < 4) {
+        // sA[kb, row0 + 64c .. +64).  The descriptor spans to the end of the
+        // scale array, so no load is partly out of range; rows past the tile
+        // edge read neighbouring scales that only reach rows never stored.
+        const int64_t off = int64_t(kt) * p.M + ti.row0 + c * 64;
         const int64_t rem = int64_t(nk) * p.M - off;
-        const Rsrc rs = make_rsrc4(p.sa + (rem > 0 ? off : 0), uint32_t(rem > 0 ? rem * 4 : 0));
-        const uint32_t voff = live ? uint32_t(lane) * 4u : 0x80000000u;
-        dma_b32(rs, lds_addr(st + A_BYTES + B_BYTES + wave * 256), voff);
-      }
-    } else {
-      if constexpr (EPI == Epi::Block128x1) {
-        // waves 0 and 1 fetch the 128 column scales; waves 2 and 3 write zeros
-        // into their own (unused) chunks
-        const int64_t off = int64_t(kt) * p.N + ti.n0 + (wave & 1) * 64;
-        const int64_t rem = int64_t(nk) * p.N - off;
-        const Rsrc rs = make_rsrc4(ti.sb + (rem > 0 ? off : 0), uint32_t(rem > 0 ? rem * 4 : 0));
-        const uint32_t voff = (live && wave < 2) ? uint32_t(lane) * 4u : 0x80000000u;
-        dma_b32(rs, lds_addr(st + A_BYTES + B_BYTES + SA_BYTES + wave * 256), voff);
-      } else if constexpr (EPI == Epi::Block128x128) {
-        // the weight-block scale of (n-block, kb): one float, fetched by lane 0 of wave 0
-        const int64_t nb = ti.n0 / 128;
-        const int64_t idx = B_KN ? int64_t(kt) * (p.N / 128) + nb : nb * nk + kt;
-        const int64_t total = int64_t(nk) * (p.N / 128);
-        const Rsrc rs = make_rsrc4(ti.sb, uint32_t(total * 4));
-        const uint32_t voff = (live && wave == 0 && lane == 0) ? uint32_t(idx) * 4u : 0x80000000u;
-        dma_b32(rs, lds_addr(st + A_BYTES + B_BYTES + SA_BYTES + wave * 256), voff);
+        const Rsrc r = make_rsrc4(p.sa + (rem > 0 ? off : 0), uint32_t(rem > 0 && live ? rem * 4 : 0));
+        dma_b32(r, st + A_BYTES + B_BYTES + c * 256, uint32_t(lane) * 4u);
+      } else {
+        const int cc = c - 4;
+        if constexpr (EPI == Epi::Block128x1) {
+          // column scales sB[kb, n0 + 64cc .. +64)
+          const bool in = live && cc * 64 < BN;
+          const int64_t off = int64_t(kt) * p.N + ti.n0 + cc * 64;
+          const int64_t rem = int64_t(nk) * p.N - off;
+          const Rsrc r = make_rsrc4(ti.sb + (rem > 0 && in ? off : 0), uint32_t(rem > 0 && in ? rem * 4 : 0));
+          dma_b32(r, st + A_BYTES + B_BYTES + SA_BYTES + cc * 256, uint32_t(lane) * 4u);
+        } else {
+          // the weight-block scale of (n-block n0/128 + cc, kb), fetched by lane 0
+          const int64_t nb = ti.n0 / 128 + cc;
+          const bool in = live && cc < BN / 128 && nb < p.N / 128;
+          const int64_t idx = B_KN ? int64_t(kt) * (p.N / 128) + nb : nb * nk + kt;
+          const Rsrc r = make_rsrc4(ti.sb + (in ? idx : 0), uint32_t(in ? 4 : 0));
+          dma_b32(r, st + A_BYTES + B_BYTES + SA_BYTES + cc * 256, uint32_t(lane) * 4u);
+        }
       }
     }
   };
@@ -359,11 +396,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
 
-  // One K step on stage (kt % STAGES).  The direct loads of K step kt + 2
-  // (zeros past the end) are spread over the fragment rows, the A fragment of
-  // the next row is read one row ahead, and sched_barrier fences pin the
-  // order (MFMA q, promotion of MFMA q-1) so that every MFMA overlaps the
-  // VALU work of its predecessor instead of waiting for it.
+  // One K step on stage S.  The loads of K step kt + D (zeros past the end)
+  // are spread over the fragment rows, the A fragment of the next row is read
+  // one row ahead, and sched_barrier fences pin the order (MFMA q, promotion
+  // of MFMA q-1) so that every MFMA overlaps the VALU work of its
+  // predecessor instead of waiting for it.
   auto compute = [&](auto stage_c, int kt, bool live_next) {
     constexpr int S = decltype(stage_c)::value;
     const uint8_t* As = stage_ptr(S);
@@ -379,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m
     [[maybe_unused]] v4f fa_cur;
     if constexpr (BLOCKWISE) {
       fa_cur = *reinterpret_cast<const v4f*>(sas + row_base + fq * 4);
-      if constexpr (EPI == Epi::Block128x128) sbk = sbs[0];
+      if constexpr (EPI == Epi::Block128x128) sbk = sbs[(col_base / 128) * 64];
       if constexpr (EPI == Epi::Block128x1) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) sbv[j] = sbs[col_base + j * 16 + frow];
@@ -390,7 +427,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int q = i * LDIRECT / FM; q < (i + 1) * LDIRECT / FM; ++q) issue_one(q, (S + 2) % STAGES, kt + 2, live_next);
+      for (int q = i * LDIRECT / FM; q < (i + 1) * LDIRECT / FM; ++q) issue_one(q, (S + D) % STAGES, kt + D, live_next);
       v8i a_next = a_cur;
       [[maybe_unused]] v4f fa_next;
       if (i + 1 < FM) {
@@ -437,33 +474,34 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m
     }
   };
 
-  // ---------------- main loop: 3-stage ring, prefetch distance 2 ----------------
+  // ---------------- main loop: STAGES-deep ring, prefetch distance D ----------------
   auto step = [&](auto stage_c, int kt) {
     constexpr int S = decltype(stage_c)::value;
-    // Stage kt is complete once only the newest step's loads are in flight.
-    // A bare s_barrier (not __syncthreads, whose release fence would drain
-    // every outstanding load): each wave first retires its own DMA for this
-    // stage and its LDS reads / writes, so after the barrier the stage is
+    // Stage kt is complete once only the newest D-1 steps' loads are in
+    // flight.  A bare s_barrier (not __syncthreads, whose release fence would
+    // drain every outstanding load): each wave first retires its own DMA for
+    // this stage and its LDS reads / writes, so after the barrier the stage is
     // complete and the stage refilled next is no longer being read.
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS) : "memory");
-    const bool live = kt + 2 < nk;
-    kn_load(kt + 2, live);
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((D - 1) * LPS) : "memory");
+    const bool live = kt + D < nk;
+    kn_load(kt + D, live);
     compute(stage_c, kt, live);
-    kn_store((S + 2) % STAGES);
+    kn_store((S + D) % STAGES);
   };
   if (nk > 0) {
 #pragma unroll
-    for (int q = 0; q < LDIRECT; ++q) issue_one(q, 0, 0, true);
-    kn_load(0, true);
-    kn_store(0);
+    for (int d = 0; d < D; ++d) {
 #pragma unroll
-    for (int q = 0; q < LDIRECT; ++q) issue_one(q, 1, 1, nk > 1);
-    kn_load(1, nk > 1);
-    kn_store(1);
-    for (int kt = 0; kt < nk; kt += 3) {
+      for (int q = 0; q < LDIRECT; ++q) issue_one(q, d, d, d < nk);
+      kn_load(d, d < nk);
+      kn_store(d);
+    }
+    for (int kt = 0; kt < nk; kt += STAGES) {
       step(std::integral_constant<int, 0>{}, kt);
       if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
-      if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
+      if constexpr (STAGES > 2) {
+        if (kt + 2 < nk) step(std::integral_constant<int, 2 % STAGES>{}, kt + 2);
+      }
     }
   }
 
@@ -472,7 +510,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m
   // step into spare stages) has landed before the stages are reused below.
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();   // every wave is done with the ring
-  uint8_t* ep = (wave < 2 ? stage0 : stage1) + (wave & 1) * TM * EPI_PITCH;
+  uint8_t* ep = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * TM * EPI_PITCH;
   [[maybe_unused]] float s_tensor = 0.f;
   if constexpr (EPI == Epi::Tensor) s_tensor = p.sa[0] * p.sb[0];
   [[maybe_unused]] float sar[FM][4];
@@ -542,7 +580,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmProblem p, int tiles_m
   }
 }
 
-template <int BM, int BN, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED>
+template <int BM, int BN, int NW, int STAGES, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
   int tiles_m, tiles_n = int((p.N + BN - 1) / BN);
   if (GROUPED)
@@ -554,17 +592,28 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
   const int grid = int((tiles + 7) / 8 * 8);
   const int outb = p.out_bf16 ? 2 : 4;
   const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, B_KN, OUT_BF16, BIAS, GROUPED>), dim3(grid), dim3(256), 0, st, p,
-                     tiles_m, tiles_n, vec_out);
+  constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
+  if (BLOCKWISE || p.K % BK == 0)
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, NW, STAGES, EPI, B_KN, OUT_BF16, BIAS, GROUPED, true>), dim3(grid),
+                       dim3(NW * 64), 0, st, p, tiles_m, tiles_n, vec_out);
+  else if constexpr (!BLOCKWISE)
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, NW, STAGES, EPI, B_KN, OUT_BF16, BIAS, GROUPED, false>), dim3(grid),
+                       dim3(NW * 64), 0, st, p, tiles_m, tiles_n, vec_out);
   return hipGetLastError();
 }
 
 template <Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED>
 hipError_t launch_epi(const GemmProblem& p, hipStream_t st) {
+  // tensorwise / rowwise: 256 x 256 tiles, 8 waves (2 per SIMD), 2 stages;
+  // blockwise: the promotion's registers do not fit two waves per SIMD, so
+  // 256 x 128 tiles, 4 waves, 3 stages; grouped: 128 x 128 tiles, 3 stages.
+  constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
   if constexpr (GROUPED)
-    return launch_cfg<128, 128, EPI, false, OUT_BF16, BIAS, true>(p, st);
+    return launch_cfg<128, 128, 4, 3, EPI, false, OUT_BF16, BIAS, true>(p, st);
+  else if constexpr (BLOCKWISE)
+    return launch_cfg<256, 128, 4, 3, EPI, B_KN, OUT_BF16, BIAS, false>(p, st);
   else
-    return launch_cfg<256, 128, EPI, B_KN, OUT_BF16, BIAS, false>(p, st);
+    return launch_cfg<256, 256, 8, 2, EPI, B_KN, OUT_BF16, BIAS, false>(p, st);
 }
 
 template <Epi EPI, bool B_KN, bool GROUPED>
