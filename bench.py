@@ -19,6 +19,7 @@ numbers for every workload, and the CPU oracle timed on a bounded sample.
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,8 +41,6 @@ def parse():
     ap.add_argument("--workload", default="blockwise_fwd_16640x5120x8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-recipes", action="store_true")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="HBM bytes per launch measured with rocprofv3 counters (optional)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device-to-device copy (3 times), so that a rocprofv3 "
                          "counter run sees FETCH_SIZE / WRITE_SIZE of a kernel with known traffic")
@@ -219,6 +218,27 @@ def cpu_baseline(workloads):
                       f"({2.0 * Ms * N * K / 1e9:.0f} GFLOP), rounding to bf16"}
 
 
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch from the committed counter summary
+    profiles/<workload>.md (FETCH_SIZE + WRITE_SIZE, each scaled by what the
+    counter reads for a plain copy of known size).  None when there is no
+    summary, or when the GEMM source has changed since the counters were taken
+    (the summary records the sha256 of gemm.hip it was measured with)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", workload + ".md")
+    src = os.path.join(ROOT, "precision_matmul_amd", "csrc", "gemm.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    got = dict(re.findall(r"^(traffic_bytes_per_launch|kernel_source_sha256): *(\S+)$", text, re.M))
+    if got.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in got:
+        return None
+    return int(got["traffic_bytes_per_launch"])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -276,13 +296,7 @@ def main():
     print(f"[bench] step {ms_step:.3f} ms, gemm {gemm_ms:.3f} ms ({achieved:.1f} TFLOP/s)", file=sys.stderr,
           flush=True)
 
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            with open(args.traffic_json) as f:
-                traffic = json.load(f).get(args.workload)
-        except (OSError, ValueError):
-            traffic = None
+    traffic = measured_traffic(args.workload)
 
     result = {
         "metric": "FP8 scaled-GEMM TFLOP/s at 1 MI355X + % of FP8 MFMA peak, per recipe",
