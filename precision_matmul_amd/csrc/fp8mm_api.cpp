@@ -12,7 +12,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/fp8mm.h"
+#include "fp8mm.h"
 #include "launch.hpp"
 
 namespace {

@@ -8,16 +8,21 @@
 // #2784 ("improve fp8 blockwise gemm perf"); the grouped form is that of
 // pytorch/ao PR #4390 ("Add _grouped_mm dispatch handler to Float8Tensor").
 //
+// This file holds the general tile kernel; it serves B stored [K, N]
+// (grad_output @ weight), the grouped (MoE) GEMM and plain GEMMs whose
+// leading dimensions are below 128 bytes.  Plain GEMMs with B stored [N, K]
+// go to the streaming kernel of gemm_sym.hip.
+//
 // Design (MI355X first):
-//  * One workgroup of 4 waves computes a BM x BN output tile; each wave a
+//  * A workgroup of WM x WN waves computes a BM x BN output tile; each wave a
 //    TM x TN sub-tile made of 16x16 fragments.  The K loop walks 128-byte
 //    steps: one v_mfma_f32_16x16x128_f8f6f4 consumes exactly one 128-wide K
 //    block, which is also the scaling block of the blockwise recipes.
 //  * A and B (B stored [N, K]) are staged global -> LDS with direct-to-LDS
-//    buffer loads (no VGPR round trip), double buffered, one barrier per K
-//    step.  LDS rows are 128 bytes; 16-byte chunk c of row r sits at slot
-//    c ^ (r & 7) so that fragment reads of 8 consecutive rows hit 8 distinct
-//    bank groups.  Buffer descriptors clip the ragged M / N / K edges to zero.
+//    buffer loads (no VGPR round trip) into a 2- or 3-stage ring, one barrier
+//    per K step.  LDS rows are 128 bytes; 16-byte chunk c of row r sits at
+//    slot c ^ ((r >> 1) & 7).  Buffer descriptors clip the ragged M / N / K
+//    edges to zero.
 //  * B stored [K, N] (grad_input's weight) is loaded to registers and
 //    byte-transposed with v_perm_b32 on its way into the same [N][128] LDS
 //    layout.
@@ -33,78 +38,13 @@
 //    64-lane prefix scan, so no host synchronization is needed.
 #include <type_traits>
 
-#include "launch.hpp"
+#include "gemm_common.hpp"
 
 namespace fp8mm {
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+using namespace gk;
 
-constexpr int BK = 128;
-
-__device__ __forceinline__ v4f mfma_16x16x128(const v8i& a, const v8i& b, const v4f& c) {
-  // Zero scale operands select the unscaled FP8 x FP8 instruction
-  // (cbsz = blgp = 0: both operands E4M3).
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// LDS tile rows are 128 bytes; 16-byte chunk c of row r is stored at slot
-// c ^ ((r >> 1) & 7).  A 16x16 fragment read has 16 lanes of 16 bytes in
-// flight per LDS cycle, one per row of a 16-row group: the swizzle gives the
-// 16 rows distinct (row parity, slot) pairs, i.e. distinct bank groups of the
-// 64-bank LDS.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Buffer descriptor as four wave-uniform dwords (base, stride 0, size in
-// bytes, gfx9 raw-buffer flags); loads at offsets >= size return zeros.
-typedef int Rsrc __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ Rsrc make_rsrc4(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return Rsrc{__builtin_amdgcn_readfirstlane(int(uint32_t(a))), __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32))),
-              __builtin_amdgcn_readfirstlane(int(bytes)), 0x00020000};
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return uint32_t(__builtin_amdgcn_readfirstlane(
-      int(uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p)))));
-}
-
-// Global -> LDS DMA of 16 (or 4) bytes per lane: lane l writes LDS bytes
-// [lds + 16 l, +16) (or [lds + 4 l, +4)).  Written as inline asm so that the
-// compiler does not attach its own conservative LDS-DMA waits to every LDS
-// read; the kernel tracks these loads itself with s_waitcnt vmcnt.  The
-// instructions have no register results: their operands are consumed at
-// issue.
-__device__ __forceinline__ void dma_b128(Rsrc r, uint32_t lds, uint32_t voff, uint32_t soff) {
-  soff = uint32_t(__builtin_amdgcn_readfirstlane(int(soff)));
-  lds = uint32_t(__builtin_amdgcn_readfirstlane(int(lds)));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(r),
-               "s"(soff)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ void dma_b32(Rsrc r, uint32_t lds, uint32_t voff) {
-  lds = uint32_t(__builtin_amdgcn_readfirstlane(int(lds)));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
-               : "memory", "m0");
-}
-
-// The same descriptor with no valid bytes: every lane's load returns zero.
-__device__ __forceinline__ Rsrc dead(Rsrc r) { return Rsrc{r.x, r.y, 0, r.w}; }
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
 
 // 4x4 byte transpose: rows r[0..3] hold 4 consecutive k for 4 n (byte n of
 // r[k]); the result c[n] holds byte k = r[k].byte(n).
@@ -119,30 +59,12 @@ __device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t c[4])
   c[3] = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
 }
 
-struct TileInfo {
-  int64_t row0;       // first output / A row of the tile
-  int rows_valid;     // rows of the tile inside the problem (<= BM)
-  int64_t n0;
-  int cols_valid;
-  const uint8_t* A;   // A + row0 * lda
-  const uint8_t* B;   // tile origin of B (n0 applied)
-  const float* sb;    // scale_b of this problem (expert applied)
-  const uint16_t* bias;
-};
-
-constexpr int epi_passes(int nw, int tm, int tn, int outb, int stage) {
-  // smallest number of column passes whose staging (nw/2 waves per stage
-  // array, TM rows each, padded pitch) fits in one stage array
-  for (int pz = 1; pz <= 4; pz *= 2)
-    if ((nw / 2) * tm * ((tn / pz) * outb + 16) <= stage) return pz;
-  return 8;
-}
-
-template <int BM, int BN, int NW, int STAGES, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED, bool K_ALIGNED>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int vec_out) {
+template <int BM, int BN, int WM, int WN, int STAGES, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED,
+          bool K_ALIGNED>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int vec_out) {
+  constexpr int NW = WM * WN;            // waves: WM along M x WN along N
   constexpr int NT = NW * 64;
-  constexpr int WN = NW / 2;             // waves: 2 along M x NW/2 along N
-  constexpr int TM = BM / 2;
+  constexpr int TM = BM / WM;
   constexpr int TN = BN / WN;
   constexpr int FM = TM / 16;
   constexpr int FN = TN / 16;
@@ -171,7 +93,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmProblem p, int til
   constexpr int LKN = B_KN ? KR : 0;
   constexpr int LS = BLOCKWISE ? 8 / NW : 0;
   constexpr int LPS = LA + LB + LKN + LS;
-  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert((NW == 4 || NW == 8) && NW % 2 == 0, "4 or 8 waves");
   static_assert(STAGES == 2 || STAGES == 3, "2 or 3 stages");
   static_assert(TM % 16 == 0 && TN % 16 == 0 && LA >= 1 && (B_KN || LB >= 1), "tile shape");
   static_assert(!BLOCKWISE || (BM == 256 && BN % 128 == 0 && 128 % TN == 0), "blockwise tile shape");
@@ -191,17 +113,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmProblem p, int til
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---------------- tile selection ----------------
-  const int per_xcd = gridDim.x / 8;   // the launcher pads the grid to a multiple of 8
-  const int lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   TileInfo ti;
   if constexpr (!GROUPED) {
-    if (lin >= tiles_m * tiles_n) return;
-    constexpr int GROUP_M = 8;
-    const int span = GROUP_M * tiles_n;
-    const int first_m = (lin / span) * GROUP_M;
-    const int gsize = min(tiles_m - first_m, GROUP_M);
-    const int tm = first_m + (lin % span) % gsize;
-    const int tn = (lin % span) / gsize;
+    int tm, tn;
+    if (!tile_coords(tiles_m, tiles_n, tm, tn)) return;
     ti.row0 = int64_t(tm) * BM;
     ti.rows_valid = int(min<int64_t>(BM, p.M - ti.row0));
     ti.n0 = int64_t(tn) * BN;
@@ -212,6 +127,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmProblem p, int til
     ti.bias = p.bias;
   } else {
     // lin = tn * tiles_m + g: the m-tiles of one expert are adjacent.
+    const int per_xcd = gridDim.x / 8;   // the launcher pads the grid to a multiple of 8
+    const int lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     const int tn = lin / tiles_m;
     const int g = lin % tiles_m;
     if (tn >= tiles_n) return;
@@ -378,8 +295,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmProblem p, int til
   };
 
   // ---------------- accumulators ----------------
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
+  const int wm = wave % WM;
+  const int wn = wave / WM;
   const int row_base = wm * TM;
   const int col_base = wn * TN;
   const int frow = lane & 15;   // fragment row (A) / column (B) of this lane
@@ -580,7 +497,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_kernel(GemmProblem p, int til
   }
 }
 
-template <int BM, int BN, int NW, int STAGES, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED>
+template <int BM, int BN, int WM, int WN, int STAGES, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
   int tiles_m, tiles_n = int((p.N + BN - 1) / BN);
   if (GROUPED)
@@ -594,11 +511,11 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
   const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
   if (BLOCKWISE || p.K % BK == 0)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, NW, STAGES, EPI, B_KN, OUT_BF16, BIAS, GROUPED, true>), dim3(grid),
-                       dim3(NW * 64), 0, st, p, tiles_m, tiles_n, vec_out);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, EPI, B_KN, OUT_BF16, BIAS, GROUPED, true>), dim3(grid),
+                       dim3(WM * WN * 64), 0, st, p, tiles_m, tiles_n, vec_out);
   else if constexpr (!BLOCKWISE)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, NW, STAGES, EPI, B_KN, OUT_BF16, BIAS, GROUPED, false>), dim3(grid),
-                       dim3(NW * 64), 0, st, p, tiles_m, tiles_n, vec_out);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, EPI, B_KN, OUT_BF16, BIAS, GROUPED, false>), dim3(grid),
+                       dim3(WM * WN * 64), 0, st, p, tiles_m, tiles_n, vec_out);
   return hipGetLastError();
 }
 
@@ -609,11 +526,15 @@ hipError_t launch_epi(const GemmProblem& p, hipStream_t st) {
   // 256 x 128 tiles, 4 waves, 3 stages; grouped: 128 x 128 tiles, 3 stages.
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
   if constexpr (GROUPED)
-    return launch_cfg<128, 128, 4, 3, EPI, false, OUT_BF16, BIAS, true>(p, st);
+    return launch_cfg<128, 128, 2, 2, 3, EPI, false, OUT_BF16, BIAS, true>(p, st);
+  else if constexpr (BLOCKWISE && B_KN)
+    return launch_cfg<256, 128, 2, 2, 3, EPI, true, OUT_BF16, BIAS, false>(p, st);   // cfg:kn_block
+  else if constexpr (B_KN)
+    return launch_cfg<256, 256, 2, 4, 2, EPI, true, OUT_BF16, BIAS, false>(p, st);   // cfg:kn_row
   else if constexpr (BLOCKWISE)
-    return launch_cfg<256, 128, 4, 3, EPI, B_KN, OUT_BF16, BIAS, false>(p, st);
+    return launch_cfg<256, 128, 2, 2, 3, EPI, false, OUT_BF16, BIAS, false>(p, st);  // cfg:block
   else
-    return launch_cfg<256, 256, 8, 2, EPI, B_KN, OUT_BF16, BIAS, false>(p, st);
+    return launch_cfg<256, 256, 2, 4, 2, EPI, false, OUT_BF16, BIAS, false>(p, st);  // cfg:row
 }
 
 template <Epi EPI, bool B_KN, bool GROUPED>
@@ -628,6 +549,8 @@ hipError_t launch_out(const GemmProblem& p, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
   if (p.offsets) return launch_out<Epi::Row, false, true>(p, st);
+  // the streaming kernel's grouped loads need leading dimensions of at least 128 bytes
+  if (!p.b_kn && p.lda >= 128 && p.ldb >= 128) return launch_gemm_streaming(p, st);
   switch (p.epi) {
     case Epi::Tensor:
       return p.b_kn ? launch_out<Epi::Tensor, true, false>(p, st) : launch_out<Epi::Tensor, false, false>(p, st);

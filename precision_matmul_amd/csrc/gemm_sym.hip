@@ -1,0 +1,422 @@
+// Streaming FP8 (E4M3) scaled GEMM for gfx950, B stored [N, K].
+//
+//   out[i, j] = sum_k A[i,k] sA(i,k) * B(j,k) sB(j,k)  (+ bias[j])
+//
+// Serves the forward (input @ weight.t()) and weight-gradient
+// (grad_output.t() @ input, both operands stored token-contiguous) call forms
+// of ColossalAI PR #6419 ("Fix: Handle LowLevelZeroPlugin with use_fp8=True",
+// "Forward pass" / "Backward pass"), for the tensorwise, rowwise, 1x128 x
+// 128x128 and 1x128 x 128x1 recipes of pytorch PR #164141 ("Add
+// _scaled_mm_v2 API") and pytorch/ao PR #2784 ("improve fp8 blockwise gemm
+// perf").
+//
+// Schedule.  A workgroup of 8 waves (two per SIMD) computes a 256 x 256
+// output tile, each wave a 64 x 128 sub-tile: 4 x 8 fragments of
+// v_mfma_f32_16x16x128_f8f6f4 (one instruction consumes one 128-wide K
+// block, which is also the scaling block of the blockwise recipes).  Both
+// waves of a SIMD issue matrix instructions all the time; a single wave
+// cannot keep the matrix pipe busy on its own.  Within a K step a wave walks
+// its 8 fragment columns; the 4 A fragments stay in registers and the B
+// fragments stream through a two-entry ring, each read one column ahead.
+// LDS reads, global -> LDS loads and the blockwise promotion are spread
+// between the MFMAs, so no wave ever has a burst of them.
+//
+// Data movement.  A and B tiles go global -> LDS with direct-to-LDS buffer
+// loads into a two-stage ring (2 x 66 KiB).  One workgroup barrier per K
+// step, before fragment column 7: every wave has then finished reading the
+// current stage (its last B fragment is read in column 6) and waited for its
+// own loads of the next stage, so after the barrier the next stage is
+// readable and the current one may be refilled.  The loads of step k+1 are
+// issued as early as that allows, so they have most of a step to land: the A
+// tile in column 7 of step k-1, the B tile and the scales in columns 0 and 1
+// of step k.  Each wave loads 32 rows of A and 32 of B with one group of
+// four 1 KiB loads (one M0 write per group).
+//
+// Fragment K order.  Lane l of an MFMA operand supplies 32 bytes that the
+// instruction treats as k in [32 q, 32 q + 32), q = l / 16.  A and B only
+// need the same k order, so each lane supplies the 16-byte chunks q and
+// q + 4 of the 128-byte row; with chunk c of row r stored at slot
+// c ^ ((r >> 1) & 7) these reads are close to conflict-free.
+#include <type_traits>
+
+#include "gemm_common.hpp"
+
+namespace fp8mm {
+namespace {
+
+using namespace gk;
+
+constexpr int SY_BM = 256;
+constexpr int SY_BN = 256;
+constexpr int SY_NW = 8;
+constexpr int SY_A = SY_BM * BK;            // A codes of one stage
+constexpr int SY_B = SY_BN * BK;            // B codes of one stage
+constexpr int SY_SCALE = 1024;              // 256 fp32 scales (sA), or up to 256 (sB)
+constexpr int SY_STAGE = SY_A + SY_B + 2 * SY_SCALE;
+constexpr int SY_TM = 64;                   // wave sub-tile
+constexpr int SY_TN = 128;
+constexpr int SY_FM = SY_TM / 16;
+constexpr int SY_FN = SY_TN / 16;
+
+__device__ __forceinline__ void sy_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+template <Epi EPI, bool OUT_BF16, bool BIAS, bool K_ALIGNED>
+__global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, int tiles_m, int tiles_n,
+                                                                   int vec_out) {
+  constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
+  constexpr int OUTB = OUT_BF16 ? 2 : 4;
+  constexpr int EPI_PASSES = epi_passes(SY_NW, SY_TM, SY_TN, OUTB, SY_STAGE);
+  constexpr int EPI_COLS = SY_TN / EPI_PASSES;
+  constexpr int EPI_PITCH = EPI_COLS * OUTB + 16;
+  static_assert(EPI_PASSES <= 4 && SY_TN % EPI_PASSES == 0, "epilogue staging");
+  static_assert(2 * SY_STAGE <= 160 * 1024, "LDS budget");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[SY_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[SY_STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  int tm, tn;
+  if (!tile_coords(tiles_m, tiles_n, tm, tn)) return;
+  const int64_t row0 = int64_t(tm) * SY_BM;
+  const int rows_valid = int(min<int64_t>(SY_BM, p.M - row0));
+  const int64_t n0 = int64_t(tn) * SY_BN;
+  const int cols_valid = int(min<int64_t>(SY_BN, p.N - n0));
+  const int K = int(p.K);
+  const int nk = (K + BK - 1) / BK;
+
+  // ---------------- loaders ----------------
+  // Wave w fills tile rows [32 w, 32 w + 32) of A and of B with one group of
+  // four loads each: load q covers rows 32 w + 8 q + l / 8 (lane l, 16 bytes
+  // at slot l % 8, which holds chunk (l % 8) ^ swz(row) = (l % 8) ^
+  // (((q & 1) << 2) | (l >> 4))), at LDS 1 KiB block 4 w + q.  The group's
+  // instruction offsets add 1024 q to both addresses, so the per-lane offset
+  // of load q is its row offset minus 1024 q (non-negative as ld >= 128).
+  const int ld_row = lane >> 3;
+  const int ch_even = (lane & 7) ^ (lane >> 4);
+  const int ch_odd = (lane & 7) ^ (4 | (lane >> 4));
+  const Rsrc rsA = make_rsrc4(p.A + row0 * p.lda, uint32_t(rows_valid) * uint32_t(p.lda));
+  const Rsrc rsB = make_rsrc4(p.B + n0 * p.ldb, uint32_t(cols_valid) * uint32_t(p.ldb));
+  const uint32_t rowA = uint32_t(wave * 32 + ld_row) * uint32_t(p.lda);
+  const uint32_t rowB = uint32_t(wave * 32 + ld_row) * uint32_t(p.ldb);
+  const uint32_t stepA = 8u * uint32_t(p.lda) - 1024u;   // per-q change of the per-lane offset
+  const uint32_t stepB = 8u * uint32_t(p.ldb) - 1024u;
+  const uint32_t lds0 = lds_addr(stage0), lds1 = lds_addr(stage1);
+
+  // The group of A (or B) loads of K step kt into the stage at LDS address st;
+  // steps past the end issue nothing.
+  auto load_group = [&](bool is_b, int kt, uint32_t st) {
+    if (kt >= nk) return;
+    const uint32_t k0 = uint32_t(kt) * BK;
+    const uint32_t rowv = is_b ? rowB : rowA;
+    const uint32_t stp = is_b ? stepB : stepA;
+    uint32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ch = (q & 1) ? ch_odd : ch_even;
+      const bool in = K_ALIGNED || int(k0) + ch * 16 < K;
+      v[q] = in ? rowv + uint32_t(ch * 16) + uint32_t(q) * stp : 0x80000000u;
+    }
+    dma_b128x4(is_b ? rsB : rsA, st + (is_b ? SY_A : 0) + wave * 4096, v[0], v[1], v[2], v[3], k0);
+  };
+  // Blockwise: scale chunk `wave` of K step kt (256 bytes, filled by this
+  // wave's 64 lanes; lanes whose offset is out of range write zeros).  Waves
+  // 0..3: sA[kt, row0 + 64 wave .. +64); waves 4..7 (128x1): sB[kt, n0 +
+  // 64 (wave - 4) .. +64); waves 4, 5 (128x128): sB[n0/128 + wave - 4,
+  // kt .. ] of which only the first element is used.  Each descriptor spans
+  // to the end of the scale array, so rows or columns past the tile edge read
+  // neighbouring scales that only reach outputs never stored, and no load is
+  // partly out of range.
+  [[maybe_unused]] const float* sc_base = nullptr;
+  [[maybe_unused]] int64_t sc_count = 0;     // elements from sc_base to the array end
+  [[maybe_unused]] int64_t sc_stride = 0;    // elements per K step
+  if constexpr (BLOCKWISE) {
+    if (wave < 4) {
+      sc_base = p.sa + row0 + wave * 64;
+      sc_count = int64_t(nk) * p.M - row0 - wave * 64;
+      sc_stride = p.M;
+    } else if constexpr (EPI == Epi::Block128x1) {
+      sc_base = p.sb + n0 + (wave - 4) * 64;
+      sc_count = int64_t(nk) * p.N - n0 - (wave - 4) * 64;
+      sc_stride = p.N;
+    } else {
+      const int64_t nb = n0 / 128 + (wave - 4);
+      const bool in = wave < 6 && nb < p.N / 128;
+      sc_base = p.sb + (in ? nb * nk : 0);
+      sc_count = in ? nk : 0;
+      sc_stride = 1;
+    }
+  }
+  [[maybe_unused]] auto load_scales = [&](int kt, uint32_t st) {
+    if (kt >= nk) return;
+    const int64_t off = int64_t(kt) * sc_stride;
+    const int64_t rem = sc_count - off;
+    const Rsrc r = make_rsrc4(sc_base + (rem > 0 ? off : 0), uint32_t(rem > 0 ? rem * 4 : 0));
+    dma_b32(r, st + SY_A + SY_B + (wave < 4 ? wave * 256 : SY_SCALE + (wave - 4) * 256), uint32_t(lane) * 4u);
+  };
+
+  // ---------------- registers ----------------
+  const int wm = wave & 3;
+  const int wn = wave >> 2;
+  const int row_base = wm * SY_TM;               // sub-tile origin within the tile
+  const int col_base = wn * SY_TN;
+  const int frow = lane & 15;                    // fragment row (A) / column (B) of this lane
+  const int fq = lane >> 4;                      // K quarter of this lane
+  v4f acc[SY_FM][SY_FN];
+#pragma unroll
+  for (int i = 0; i < SY_FM; ++i)
+#pragma unroll
+    for (int j = 0; j < SY_FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto read_frag = [&](const uint8_t* tile, int r) {
+    const v4i lo = *reinterpret_cast<const v4i*>(tile + lds_off(r, fq));
+    const v4i hi = *reinterpret_cast<const v4i*>(tile + lds_off(r, fq + 4));
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  auto stage_ptr = [&](int s) -> const uint8_t* { return s == 0 ? stage0 : stage1; };
+  // Blockwise: per-lane scales of the 4 row fragments (sA of the lane's 4
+  // rows) and the B scales (128x128: the block scale, folded into the row
+  // factors in column 0 of the step that uses them; 128x1: one per column).
+  auto read_fa = [&](const uint8_t* st, v4f* fa_out, float* sbv_out) {
+    const float* sas = reinterpret_cast<const float*>(st + SY_A + SY_B);
+    const float* sbs = sas + SY_SCALE / 4;
+#pragma unroll
+    for (int i = 0; i < SY_FM; ++i) fa_out[i] = *reinterpret_cast<const v4f*>(sas + row_base + i * 16 + fq * 4);
+    if constexpr (EPI == Epi::Block128x128) {
+      sbv_out[0] = sbs[(col_base / 128) * 64];
+    } else if constexpr (EPI == Epi::Block128x1) {
+#pragma unroll
+      for (int j = 0; j < SY_FN; ++j) sbv_out[j] = sbs[col_base + j * 16 + frow];
+    }
+  };
+
+  v8i a[SY_FM];
+  v8i bring[2];
+  [[maybe_unused]] v4f fa[2][SY_FM];           // promotion factors of the current / next step
+  [[maybe_unused]] float sbv[2][SY_FN];
+  // Blockwise promotion runs two MFMAs behind: pending results and where they go.
+  [[maybe_unused]] v4f pend_t[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+  [[maybe_unused]] v4f pend_f[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+
+  // ---------------- one K step ----------------
+  // F selects the promotion-factor buffer of this step (steps alternate).
+  auto step = [&](auto stage_c, auto fsel_c, int kt) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr int F = decltype(fsel_c)::value;
+    const uint8_t* As = stage_ptr(S);
+    const uint8_t* Bs = As + SY_A;
+    const uint8_t* An = stage_ptr(S ^ 1);
+    const uint32_t this_st = S == 0 ? lds0 : lds1;
+    const uint32_t next_st = S == 0 ? lds1 : lds0;
+#pragma unroll
+    for (int j = 0; j < SY_FN; ++j) {
+      if (j == SY_FN - 1) {
+        // Barrier: every wave has read the last B fragment of this stage (in
+        // column 6) and its own loads of the next stage have landed.
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        sy_fence();
+        asm volatile("s_barrier" ::: "memory");
+        sy_fence();
+      }
+#pragma unroll
+      for (int i = 0; i < SY_FM; ++i) {
+        const int m = j * SY_FM + i;     // slot in the step
+        const v8i& bf = bring[j & 1];
+        if constexpr (!BLOCKWISE) {
+          acc[i][j] = mfma_16x16x128(a[i], bf, acc[i][j]);
+        } else {
+          const v4f t = mfma_16x16x128(a[i], bf, v4f{0.f, 0.f, 0.f, 0.f});
+          // promote the result of slot m - 2 (possibly of the previous step)
+          {
+            const int mp = m - 2;
+            const int ip = (mp + 32) % 32 % SY_FM;
+            const int jp = (mp + 32) % 32 / SY_FM;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[ip][jp][e] = __builtin_fmaf(pend_t[m & 1][e], pend_f[m & 1][e], acc[ip][jp][e]);
+            asm volatile("" ::"v"(acc[ip][jp]));
+          }
+          pend_t[m & 1] = t;
+          if constexpr (EPI == Epi::Block128x128) {
+            if (j == 0) fa[F][i] = fa[F][i] * sbv[F][0];
+            pend_f[m & 1] = fa[F][i];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pend_f[m & 1][e] = fa[F][i][e] * sbv[F][j];
+          }
+        }
+        if constexpr (BLOCKWISE) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        sy_fence();
+        // ---- work between MFMAs ----
+        // B fragment of the next column (column 7: column 0 of the next step)
+        if (i == 0) {
+          if (j + 1 < SY_FN) {
+            bring[(j + 1) & 1] = read_frag(Bs, col_base + (j + 1) * 16 + frow);
+          } else {
+            bring[0] = read_frag(An + SY_A, col_base + frow);
+          }
+        }
+        // next step's A fragment i, right after its last use
+        if (j == SY_FN - 1) a[i] = read_frag(An, row_base + i * 16 + frow);
+        // next step's promotion factors
+        if constexpr (BLOCKWISE) {
+          if (j == SY_FN - 1 && i == 1) read_fa(An, fa[F ^ 1], sbv[F ^ 1]);
+        }
+        // loads: A of step kt+2 into this stage (free after the barrier) in
+        // column 7; B and the scales of step kt+1 into the other stage in
+        // columns 0 and 1
+        if (j == SY_FN - 1 && i == 0) load_group(false, kt + 2, this_st);
+        if (j == 0 && i == 1) load_group(true, kt + 1, next_st);
+        if constexpr (BLOCKWISE) {
+          if (j == 1 && i == 1) load_scales(kt + 1, next_st);
+        }
+        sy_fence();
+      }
+    }
+  };
+
+  if (nk > 0) {
+    // Prologue: stage 0 complete and visible; the fragments and factors of
+    // step 0 in registers; the first loads of step 1 in flight.
+    load_group(false, 0, lds0);
+    load_group(true, 0, lds0);
+    if constexpr (BLOCKWISE) load_scales(0, lds0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < SY_FM; ++i) a[i] = read_frag(stage0, row_base + i * 16 + frow);
+    bring[0] = read_frag(stage0 + SY_A, col_base + frow);
+    if constexpr (BLOCKWISE) read_fa(stage0, fa[0], sbv[0]);
+    load_group(false, 1, lds1);
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, kt + 1);
+    }
+    if constexpr (BLOCKWISE) {
+      // the last two results of the last step
+#pragma unroll
+      for (int mm = 30; mm < 32; ++mm) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[mm % SY_FM][mm / SY_FM][e] = __builtin_fmaf(pend_t[mm & 1][e], pend_f[mm & 1][e], acc[mm % SY_FM][mm / SY_FM][e]);
+      }
+    }
+  }
+
+  // ---------------- epilogue: scale, round, stage in LDS, 16-byte stores ----------------
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+  uint8_t* ep = (wave < SY_NW / 2 ? stage0 : stage1) + (wave % (SY_NW / 2)) * SY_TM * EPI_PITCH;
+  [[maybe_unused]] float s_tensor = 0.f;
+  if constexpr (EPI == Epi::Tensor) s_tensor = p.sa[0] * p.sb[0];
+  [[maybe_unused]] float sar[SY_FM][4];
+  if constexpr (EPI == Epi::Row) {
+#pragma unroll
+    for (int i = 0; i < SY_FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rt = row_base + i * 16 + fq * 4 + e;
+        sar[i][e] = rt < rows_valid ? p.sa[row0 + rt] : 0.f;
+      }
+  }
+#pragma unroll
+  for (int pass = 0; pass < EPI_PASSES; ++pass) {
+    constexpr int FNP = SY_FN / EPI_PASSES;
+#pragma unroll
+    for (int jj = 0; jj < FNP; ++jj) {
+      const int j = pass * FNP + jj;
+      const int cl = jj * 16 + frow;
+      const int ct = col_base + j * 16 + frow;
+      const bool cin = ct < cols_valid;
+      [[maybe_unused]] float sbc = 0.f;
+      if constexpr (EPI == Epi::Row) sbc = cin ? p.sb[n0 + ct] : 0.f;
+      float bias_v = 0.f;
+      if constexpr (BIAS) bias_v = cin ? __uint_as_float(uint32_t(p.bias[n0 + ct]) << 16) : 0.f;
+#pragma unroll
+      for (int i = 0; i < SY_FM; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = acc[i][j][e];
+          if constexpr (EPI == Epi::Tensor) v = v * s_tensor;
+          if constexpr (EPI == Epi::Row) v = (v * sar[i][e]) * sbc;
+          if constexpr (BIAS) v = v + bias_v;
+          uint8_t* dst = ep + (i * 16 + fq * 4 + e) * EPI_PITCH + cl * OUTB;
+          if constexpr (OUT_BF16)
+            *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_rne(v);
+          else
+            *reinterpret_cast<float*>(dst) = v;
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CPR = EPI_COLS * OUTB / 16;
+    constexpr int EPR = 16 / OUTB;
+#pragma unroll 4
+    for (int idx = lane; idx < SY_TM * CPR; idx += 64) {
+      const int rl = idx / CPR;
+      const int ch = idx % CPR;
+      const int rt = row_base + rl;
+      const int ct = col_base + pass * EPI_COLS + ch * EPR;
+      if (rt >= rows_valid || ct >= cols_valid) continue;
+      const uint8_t* src = ep + rl * EPI_PITCH + ch * 16;
+      uint8_t* dst = reinterpret_cast<uint8_t*>(p.out) + ((row0 + rt) * p.ldo + n0 + ct) * OUTB;
+      if (vec_out && ct + EPR <= cols_valid) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        const int n = min(EPR, cols_valid - ct);
+        for (int e = 0; e < n; ++e) {
+          if constexpr (OUT_BF16)
+            reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+          else
+            reinterpret_cast<float*>(dst)[e] = reinterpret_cast<const float*>(src)[e];
+        }
+      }
+    }
+    if (pass + 1 < EPI_PASSES) __syncthreads();
+  }
+}
+
+template <Epi EPI, bool OUT_BF16, bool BIAS>
+hipError_t launch_sym(const GemmProblem& p, hipStream_t st) {
+  const int tiles_m = int((p.M + SY_BM - 1) / SY_BM);
+  const int tiles_n = int((p.N + SY_BN - 1) / SY_BN);
+  const int64_t tiles = int64_t(tiles_m) * tiles_n;
+  if (tiles == 0) return hipSuccess;
+  const int grid = int((tiles + 7) / 8 * 8);
+  const int outb = OUT_BF16 ? 2 : 4;
+  const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
+  constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
+  if (BLOCKWISE || p.K % BK == 0)
+    hipLaunchKernelGGL((gemm_sym_kernel<EPI, OUT_BF16, BIAS, true>), dim3(grid), dim3(SY_NW * 64), 0, st, p, tiles_m,
+                       tiles_n, vec_out);
+  else if constexpr (!BLOCKWISE)
+    hipLaunchKernelGGL((gemm_sym_kernel<EPI, OUT_BF16, BIAS, false>), dim3(grid), dim3(SY_NW * 64), 0, st, p, tiles_m,
+                       tiles_n, vec_out);
+  return hipGetLastError();
+}
+
+template <Epi EPI>
+hipError_t launch_sym_out(const GemmProblem& p, hipStream_t st) {
+  const bool bias = p.bias != nullptr;
+  if (p.out_bf16) return bias ? launch_sym<EPI, true, true>(p, st) : launch_sym<EPI, true, false>(p, st);
+  return bias ? launch_sym<EPI, false, true>(p, st) : launch_sym<EPI, false, false>(p, st);
+}
+
+}  // namespace
+
+// Plain (non-grouped) GEMM with B stored [N, K], streaming schedule.
+hipError_t launch_gemm_streaming(const GemmProblem& p, hipStream_t st) {
+  switch (p.epi) {
+    case Epi::Tensor: return launch_sym_out<Epi::Tensor>(p, st);
+    case Epi::Row: return launch_sym_out<Epi::Row>(p, st);
+    case Epi::Block128x128: return launch_sym_out<Epi::Block128x128>(p, st);
+    case Epi::Block128x1: return launch_sym_out<Epi::Block128x1>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fp8mm

@@ -40,5 +40,7 @@ struct GemmProblem {
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st);
+// Non-grouped GEMM with B stored [N, K] (streaming schedule, 256 x 256 tiles).
+hipError_t launch_gemm_streaming(const GemmProblem& p, hipStream_t st);
 
 }  // namespace fp8mm
