@@ -188,6 +188,8 @@ fp8mm_status fp8_scaled_mm(const uint8_t* A, int64_t M, int64_t K, int64_t lda, 
   p.out_bf16 = out_dtype == FP8MM_OUT_BF16;
   p.offsets = nullptr;
   p.E = 0;
+  p.row_begin = 0;
+  p.row_end = M;
   return from_hip(fp8mm::launch_gemm(p, stream), "fp8_scaled_mm");
 }
 
@@ -224,6 +226,8 @@ fp8mm_status fp8_scaled_grouped_mm(const uint8_t* A, int64_t M_total, int64_t K,
   p.out_bf16 = out_dtype == FP8MM_OUT_BF16;
   p.offsets = offsets;
   p.E = E;
+  p.row_begin = 0;
+  p.row_end = M_total;
   return from_hip(fp8mm::launch_gemm(p, stream), "fp8_scaled_grouped_mm");
 }
 

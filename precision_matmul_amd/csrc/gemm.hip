@@ -96,7 +96,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
   static_assert((NW == 4 || NW == 8) && NW % 2 == 0, "4 or 8 waves");
   static_assert(STAGES == 2 || STAGES == 3, "2 or 3 stages");
   static_assert(TM % 16 == 0 && TN % 16 == 0 && LA >= 1 && (B_KN || LB >= 1), "tile shape");
-  static_assert(!BLOCKWISE || (BM == 256 && BN % 128 == 0 && 128 % TN == 0), "blockwise tile shape");
+  static_assert(!BLOCKWISE || ((BM == 128 || BM == 256) && BN % 128 == 0 && 128 % TN == 0), "blockwise tile shape");
   static_assert(!B_KN || KR == 4 || KR == 8, "KN loader shape");
   static_assert(STAGES * STAGE <= 160 * 1024, "LDS budget");
   static_assert(EPI_PASSES <= 4 && TN % EPI_PASSES == 0, "epilogue staging");
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
   if constexpr (!GROUPED) {
     int tm, tn;
     if (!tile_coords(tiles_m, tiles_n, tm, tn)) return;
-    ti.row0 = int64_t(tm) * BM;
+    ti.row0 = p.row_begin + int64_t(tm) * BM;
     ti.rows_valid = int(min<int64_t>(BM, p.M - ti.row0));
     ti.n0 = int64_t(tn) * BN;
     ti.cols_valid = int(min<int64_t>(BN, p.N - ti.n0));
@@ -503,7 +503,7 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
   if (GROUPED)
     tiles_m = int((p.M + BM - 1) / BM + p.E);   // upper bound on expert m-tiles
   else
-    tiles_m = int((p.M + BM - 1) / BM);
+    tiles_m = int((p.row_end - p.row_begin + BM - 1) / BM);
   const int64_t tiles = int64_t(tiles_m) * tiles_n;
   if (tiles == 0) return hipSuccess;
   const int grid = int((tiles + 7) / 8 * 8);
@@ -545,12 +545,70 @@ hipError_t launch_out(const GemmProblem& p, hipStream_t st) {
   return bias ? launch_epi<EPI, B_KN, false, true, GROUPED>(p, st) : launch_epi<EPI, B_KN, false, false, GROUPED>(p, st);
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// The tail rows of a plain [N, K] GEMM.  A short tail (its 128 x 128 tiles
+// fit in half the compute units) uses 128 x 128 tiles on 4 waves, four
+// workgroups per 256 x 256 tile; a longer one 256 x 128 tiles on 8 waves,
+// which run closer to the streaming kernel's rate.
+template <Epi EPI, bool OUT_BF16, bool BIAS>
+hipError_t launch_tail(const GemmProblem& p, bool small, hipStream_t st) {
+  if (small) return launch_cfg<128, 128, 2, 2, 3, EPI, false, OUT_BF16, BIAS, false>(p, st);
+  return launch_cfg<256, 128, 4, 2, 3, EPI, false, OUT_BF16, BIAS, false>(p, st);
+}
+
+template <Epi EPI>
+hipError_t launch_tail_out(const GemmProblem& p, bool small, hipStream_t st) {
+  const bool bias = p.bias != nullptr;
+  if (p.out_bf16)
+    return bias ? launch_tail<EPI, true, true>(p, small, st) : launch_tail<EPI, true, false>(p, small, st);
+  return bias ? launch_tail<EPI, false, true>(p, small, st) : launch_tail<EPI, false, false>(p, small, st);
+}
+
+hipError_t launch_gemm_tail(const GemmProblem& p, bool small, hipStream_t st) {
+  switch (p.epi) {
+    case Epi::Tensor: return launch_tail_out<Epi::Tensor>(p, small, st);
+    case Epi::Row: return launch_tail_out<Epi::Row>(p, small, st);
+    case Epi::Block128x128: return launch_tail_out<Epi::Block128x128>(p, small, st);
+    case Epi::Block128x1: return launch_tail_out<Epi::Block128x1>(p, small, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
   if (p.offsets) return launch_out<Epi::Row, false, true>(p, st);
-  // the streaming kernel's grouped loads need leading dimensions of at least 128 bytes
-  if (!p.b_kn && p.lda >= 128 && p.ldb >= 128) return launch_gemm_streaming(p, st);
+  // The streaming kernel's grouped loads need leading dimensions of at least
+  // 128 bytes.  Its 256 x 256 tiles are handed out in rounds of one per CU;
+  // when the last round would be less than half full, the streaming kernel
+  // takes the rows of tiles that fill whole rounds and the rest of the rows
+  // (the tail) run with 128 x 128 tiles, four times as many workgroups.
+  if (!p.b_kn && p.lda >= 128 && p.ldb >= 128) {
+    const int64_t tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
+    const int64_t tiles = tiles_m * tiles_n, cus = device_cus();
+    const int64_t rem = tiles % cus;
+    const int64_t tm_main = tiles > cus && rem > 0 && rem <= cus / 2 ? (tiles / cus * cus) / tiles_n : tiles_m;
+    if (tm_main >= tiles_m || tm_main == 0) return launch_gemm_streaming(p, st);
+    GemmProblem head = p, tail = p;
+    head.row_end = tm_main * 256;
+    tail.row_begin = tm_main * 256;
+    const hipError_t e = launch_gemm_streaming(head, st);
+    if (e != hipSuccess) return e;
+    const int64_t tail_tiles = (tiles_m - tm_main) * tiles_n;
+    return launch_gemm_tail(tail, 4 * tail_tiles <= cus / 2, st);
+  }
   switch (p.epi) {
     case Epi::Tensor:
       return p.b_kn ? launch_out<Epi::Tensor, true, false>(p, st) : launch_out<Epi::Tensor, false, false>(p, st);

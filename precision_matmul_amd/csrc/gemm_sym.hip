@@ -80,7 +80,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
 
   int tm, tn;
   if (!tile_coords(tiles_m, tiles_n, tm, tn)) return;
-  const int64_t row0 = int64_t(tm) * SY_BM;
+  const int64_t row0 = p.row_begin + int64_t(tm) * SY_BM;
   const int rows_valid = int(min<int64_t>(SY_BM, p.M - row0));
   const int64_t n0 = int64_t(tn) * SY_BN;
   const int cols_valid = int(min<int64_t>(SY_BN, p.N - n0));
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
 
 template <Epi EPI, bool OUT_BF16, bool BIAS>
 hipError_t launch_sym(const GemmProblem& p, hipStream_t st) {
-  const int tiles_m = int((p.M + SY_BM - 1) / SY_BM);
+  const int tiles_m = int((p.row_end - p.row_begin + SY_BM - 1) / SY_BM);
   const int tiles_n = int((p.N + SY_BN - 1) / SY_BN);
   const int64_t tiles = int64_t(tiles_m) * tiles_n;
   if (tiles == 0) return hipSuccess;

@@ -37,6 +37,9 @@ struct GemmProblem {
   // grouped (MoE) problems
   const int32_t* offsets; // device [E] end offsets, or null for a plain GEMM
   int64_t E;
+  // plain problems: the launch covers output rows [row_begin, row_end)
+  int64_t row_begin;
+  int64_t row_end;
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st);

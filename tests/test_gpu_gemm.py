@@ -139,6 +139,45 @@ def test_blockwise_grad_weight(T, N_out, K_in):
                   f"blockwise grad_weight {N_out}x{K_in}x{T}")
 
 
+# More 256 x 256 output tiles than compute units, with a short last round:
+# the streaming kernel takes the tile rows that fill whole rounds and the
+# remaining (ragged) rows run on smaller tiles.  On a 256-CU device M = 4400
+# gives 18 x 16 tiles and a 32-tile tail (128 x 128 tail tiles), M = 5008
+# gives 20 x 16 tiles and a 64-tile tail (256 x 128 tail tiles); elsewhere
+# the same shapes still check the full result.
+@pytest.mark.parametrize("M", [4400, 5008])
+@pytest.mark.parametrize("recipe", ["tensorwise", "rowwise", "blockwise", "grad_weight"])
+def test_split_tail_rows(recipe, M):
+    N, K = 4096, 256
+    if recipe == "grad_weight":
+        inp = workloads.grad_weight(T=K, N_out=M, K_in=N, seed=77)
+        qg, sg, rg, rsg = _quant_both(inp["grad_output"], "128x1", transpose_out=True)
+        qx, sx, rx, rsx = _quant_both(inp["input"], "128x1", transpose_out=True)
+        out = fp8mm.fp8_linear_grad_weight(qg, sg, qx, sx)
+        ref = gemm.linear_grad_weight(rg, rsg, rx, rsx, out_dtype=None)
+    elif recipe == "blockwise":
+        inp = workloads.blockwise(M=M, N=N, K=K, seed=78)
+        qa, sa, ra, rsa = _quant_both(inp["input"], "1x128")
+        qb, sb, rb, rsb = _quant_both(inp["weight"], "128x128")
+        out = fp8mm.fp8_linear_forward(qa, sa, "1x128", qb, sb, "128x128")
+        ref = gemm.linear_forward(ra, rsa, "1x128", rb, rsb, "128x128", out_dtype=None)
+    elif recipe == "rowwise":
+        inp = workloads.rowwise(M=M, N=N, K=K, seed=79)
+        qa, sa, ra, rsa = _quant_both(inp["x"], "rowwise")
+        qb, sb, rb, rsb = _quant_both(inp["w"], "rowwise")
+        bias = bf16_dev(inp["bias"])
+        out = fp8mm.fp8_scaled_mm(qa, qb, sa, "rowwise", sb, "rowwise", bias=bias)
+        ref = gemm.scaled_mm(ra, rb, rsa, "rowwise", rsb, "rowwise", bias=quant.bf16_to_f32(inp["bias"]),
+                             out_dtype=None)
+    else:
+        inp = workloads.tensorwise(n=N, m=M, k=K, seed=80)
+        qa, sa, ra, rsa = _quant_both(inp["A"], "tensorwise")
+        qb, sb, rb, rsb = _quant_both(inp["B"], "tensorwise")
+        out = fp8mm.fp8_scaled_mm(qa, qb, sa, "tensorwise", sb, "tensorwise")
+        ref = gemm.scaled_mm(ra, rb, rsa, "tensorwise", rsb, "tensorwise", out_dtype=None)
+    _assert_close(out_f64(out), ref, f"split tail {recipe} {M}x{N}x{K}")
+
+
 def _grouped_case(E, N, K, sizes, seed):
     g = workloads.streams(seed, 2)
     M = int(np.sum(sizes))
