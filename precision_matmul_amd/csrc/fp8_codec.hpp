@@ -1,11 +1,13 @@
-// FP8 E4M3 ("e4m3fn") encoding and the exact quotient used by the quantizers.
+// Scale and exact quotient of the FP8 E4M3 ("e4m3fn") quantizers.
 //
-// Encoding: round to nearest, ties to an even mantissa, saturating to +-448,
-// sign bit taken from the input (OCP 8-bit floating point specification,
-// E4M3; the pages name the format only as "FP8").
+// A group's scale is s = fl32(amax / 448) (+ eps for the per-token recipe),
+// and each value becomes the E4M3 code of the correctly rounded float32
+// quotient fl32(x / s).  (The encoding itself, round to nearest even with
+// saturation to +-448 per the OCP 8-bit floating point specification, is done
+// by the hardware conversion in the kernels.)
 //
-// Everything here is __host__ __device__ so that a host build can sweep every
-// float32 bit pattern through exactly the code the kernels run.
+// Everything here is __host__ __device__ so that a host build can check the
+// quotient against IEEE division on any float32 input.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,31 +31,6 @@ FP8MM_HD float bits_f32(uint32_t u) {
 }
 
 FP8MM_HD float bf16_to_f32(uint16_t h) { return bits_f32(uint32_t(h) << 16); }
-
-// E4M3 code of |v| (bit 7 clear), v a float32 magnitude in any range.
-//   |v| >= 2^-6 : keep 3 mantissa bits with round-to-nearest-even on the
-//                 float32 bit pattern, rebias the exponent (127 -> 7); any
-//                 carry moves into the exponent, which is the next code.
-//   |v| <  2^-6 : subnormal codes are m * 2^-9, so the code is |v| * 2^9
-//                 rounded to the nearest integer, ties to even (0..8; 8 is
-//                 the smallest normal code 0x08, so the two ranges meet).
-//   Results above 0x7E (448) saturate to 0x7E; NaN maps to 0x7F.
-FP8MM_HD uint32_t e4m3_magnitude_code(uint32_t abs_bits) {
-  const uint32_t a = abs_bits;
-  const uint32_t rounded = a + 0x7FFFFu + ((a >> 20) & 1u);
-  const uint32_t normal = (rounded >> 20) - (120u << 3);
-  const float sub_f = __builtin_rintf(bits_f32(a) * 512.0f);
-  const uint32_t sub = uint32_t(sub_f);
-  uint32_t c = a >= 0x3C800000u ? normal : sub;
-  c = c > 0x7Eu ? 0x7Eu : c;
-  return a > 0x7F800000u ? 0x7Fu : c;
-}
-
-// Full code of a float32 whose sign is given separately (sign_src's sign bit).
-FP8MM_HD uint32_t e4m3_encode(float mag_src, float sign_src) {
-  const uint32_t a = f32_bits(mag_src) & 0x7FFFFFFFu;
-  return e4m3_magnitude_code(a) | ((f32_bits(sign_src) >> 24) & 0x80u);
-}
 
 // Scales smaller than this take the plain IEEE division path below.
 constexpr float kFastDivMinScale = 8.077935669463161e-28f;  // 2^-90
@@ -95,11 +72,6 @@ FP8MM_HD CastScale make_cast_scale(float s) {
   c.r = 1.0f / s;
   c.fast = s >= kFastDivMinScale;
   return c;
-}
-
-FP8MM_HD uint32_t quantize_one(float x, const CastScale& cs) {
-  const float y = cs.fast ? div_by_scale(x, cs.s, cs.r) : x / cs.s;
-  return e4m3_encode(y, x);
 }
 
 }  // namespace fp8mm

@@ -60,23 +60,56 @@ __device__ __forceinline__ uint32_t group16_max(uint32_t v) {
   return v;
 }
 
+// E4M3 codes of four quotients y = x / s, packed little-endian: round to
+// nearest even, saturating to +-448, sign taken from the input x (so that
+// -0 and negatives that round to zero give 0x80; the FMA steps of the
+// quotient can turn -0 into +0).  The hardware conversion rounds to nearest
+// even and agrees with that rule on every float32 of magnitude up to 464;
+// clamping larger magnitudes to 448 first (the comparison is false for NaN,
+// which stays NaN) extends it to the whole range.
+__device__ __forceinline__ float sat448(float y, float x) {
+  const float a = __builtin_fabsf(y);
+  return __builtin_copysignf(a > 448.0f ? 448.0f : a, x);
+}
+__device__ __forceinline__ uint32_t pack4(const float* y, const float* x, int stride = 1) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(y[0], x[0]), sat448(y[stride], x[stride]), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(y[2 * stride], x[2 * stride]), sat448(y[3 * stride], x[3 * stride]), w,
+                                      true);
+  return uint32_t(w);
+}
+
+// Quotients fl32(x / s) of 8 values, each with its own cast constants.  The
+// exact reciprocal-and-correction path covers every scale >= 2^-90; a wave
+// with any smaller scale takes the IEEE division for those values.  The test
+// is wave-uniform, so the common case has no per-value branches.
+__device__ __forceinline__ void quotients8(const float x[8], const CastScale* const cs[8], float y[8]) {
+  bool fast = true;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) fast = fast && cs[k]->fast;
+  if (__all(fast)) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = div_by_scale(x[k], cs[k]->s, cs[k]->r);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = cs[k]->fast ? div_by_scale(x[k], cs[k]->s, cs[k]->r) : x[k] / cs[k]->s;
+  }
+}
+
+__device__ __forceinline__ void unpack8(const U16x8& v, float x[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bits_f32(v.w[i] << 16);
+    x[2 * i + 1] = bits_f32(v.w[i] & 0xFFFF0000u);
+  }
+}
+
 // Encode 8 bf16 values with one scale into 8 codes (little-endian bytes).
 __device__ __forceinline__ uint2 cast8(const U16x8& v, const CastScale& cs) {
-  uint32_t out[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t pair = v.w[h * 2 + j];
-      const float x0 = bits_f32(pair << 16);
-      const float x1 = bits_f32(pair & 0xFFFF0000u);
-      word |= quantize_one(x0, cs) << (16 * j);
-      word |= quantize_one(x1, cs) << (16 * j + 8);
-    }
-    out[h] = word;
-  }
-  return make_uint2(out[0], out[1]);
+  float x[8], y[8];
+  unpack8(v, x);
+  const CastScale* c[8] = {&cs, &cs, &cs, &cs, &cs, &cs, &cs, &cs};
+  quotients8(x, c, y);
+  return make_uint2(pack4(y, x), pack4(y + 4, x + 4));
 }
 
 // ---------------------------------------------------------------------------
@@ -270,30 +303,24 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(
     cs[j].r = col_r[cc * 8 + j];
     cs[j].fast = cs[j].s >= kFastDivMinScale;
   }
+  // xs[i][j], y[i][j]: value and quotient of row r0 + i, column c0 + j
+  // (column scale j)
+  float xs[8][8], y[8][8];
+  const CastScale* c[8] = {&cs[0], &cs[1], &cs[2], &cs[3], &cs[4], &cs[5], &cs[6], &cs[7]};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    unpack8(v[i], xs[i]);
+    quotients8(xs[i], c, y[i]);
+  }
   if (!TRANSPOSE) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t out[2] = {0, 0};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t pair = v[i].w[j >> 1];
-        const float xv = bits_f32((j & 1) ? (pair & 0xFFFF0000u) : (pair << 16));
-        out[j >> 2] |= quantize_one(xv, cs[j]) << (8 * (j & 3));
-      }
-      *reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0) = make_uint2(out[0], out[1]);
-    }
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0) = make_uint2(pack4(y[i], xs[i]), pack4(y[i] + 4, xs[i] + 4));
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t out[2] = {0, 0};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t pair = v[i].w[j >> 1];
-        const float xv = bits_f32((j & 1) ? (pair & 0xFFFF0000u) : (pair << 16));
-        out[i >> 2] |= quantize_one(xv, cs[j]) << (8 * (i & 3));
-      }
-      *reinterpret_cast<uint2*>(q + (c0 + j) * ld_q + r0) = make_uint2(out[0], out[1]);
-    }
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint2*>(q + (c0 + j) * ld_q + r0) =
+          make_uint2(pack4(&y[0][j], &xs[0][j], 8), pack4(&y[4][j], &xs[4][j], 8));
   }
 }
 
