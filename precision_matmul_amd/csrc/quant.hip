@@ -165,44 +165,61 @@ __global__ __launch_bounds__(256) void quant_rowwise_long_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Blockwise (1, 128): 16 lanes per group.  A workgroup owns 16 consecutive
-// rows (4 per wave, one per 16-lane group) and walks the 128-column blocks,
-// four at a time so that four loads per lane are in flight.  Scales go to
-// scale[kb * rows + row]: 16 consecutive rows -> 64 contiguous bytes.
+// Blockwise (1, 128): one wave per row, 16 lanes per 128-column group, so a
+// wave's load covers 512 contiguous columns (4 groups).  Workgroups of 4
+// rows keep the grid fine-grained (every CU gets nearly the same number of
+// rows).  Groups of U such 512-column strips are cast from one buffer while
+// the next buffer's loads are in flight.  Scales go to scale[kb * rows + row].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_1x128_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  if (row >= rows) return;   // whole 16-lane groups leave together
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;   // whole waves leave together
   const int sub = lane & 15;
+  const int grp = lane >> 4;                     // which of the 4 groups of a strip
   const int64_t nkb = cols / 128;
-  const uint16_t* xr = x + row * ld_x + sub * 8;
-  uint8_t* qr = q + row * ld_q + sub * 8;
-  constexpr int U = 4;
-  int64_t kb = 0;
-  for (; kb + U <= nkb; kb += U) {
-    U16x8 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = load16(xr + (kb + u) * 128);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t m = group16_max(absmax8(v[u]));
-      const float s = scale_from_amax(bf16_to_f32(uint16_t(m)), 0.0f, false);
-      const CastScale cs = make_cast_scale(s);
-      if (sub == 0) scale[(kb + u) * rows + row] = s;
-      *reinterpret_cast<uint2*>(qr + (kb + u) * 128) = cast8(v[u], cs);
-    }
-  }
-  for (; kb < nkb; ++kb) {
-    const U16x8 v = load16(xr + kb * 128);
+  uint8_t* qr = q + row * ld_q + lane * 8;
+  auto cast_group = [&](const U16x8& v, int64_t strip) {
+    const int64_t kb = strip * 4 + grp;
     const uint32_t m = group16_max(absmax8(v));
     const float s = scale_from_amax(bf16_to_f32(uint16_t(m)), 0.0f, false);
     const CastScale cs = make_cast_scale(s);
-    if (sub == 0) scale[kb * rows + row] = s;
-    *reinterpret_cast<uint2*>(qr + kb * 128) = cast8(v, cs);
+    if (kb < nkb) {
+      if (sub == 0) scale[kb * rows + row] = s;
+      *reinterpret_cast<uint2*>(qr + strip * 512) = cast8(v, cs);
+    }
+  };
+  const int64_t nstrip = (nkb + 3) / 4;           // the last strip may hold 1..4 groups
+  constexpr int U = 4;
+  const int64_t nfull = nstrip / U * U;
+  // Loads past the end of a row (the last strip's missing groups, or the
+  // re-read of strip nstrip - 1 that keeps loads out of branches) are clamped
+  // into the row: they read valid columns whose results are unused.
+  auto load_strip = [&](int64_t strip) {
+    const int64_t st = min(strip, nstrip - 1);
+    const int64_t col = min(st * 512 + lane * 8, (nkb - 1) * 128 + sub * 8);
+    return load16(x + row * ld_x + col);
+  };
+  U16x8 va[U], vb[U];
+  if (nfull > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) va[u] = load_strip(u);
   }
+  for (int64_t st = 0; st < nfull; st += 2 * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) vb[u] = load_strip(st + U + u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) cast_group(va[u], st + u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) va[u] = load_strip(st + 2 * U + u);
+    if (st + U < nfull) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) cast_group(vb[u], st + U + u);
+    }
+  }
+  for (int64_t st = nfull; st < nstrip; ++st) cast_group(load_strip(st), st);
 }
 
 // ---------------------------------------------------------------------------
@@ -411,7 +428,7 @@ hipError_t launch_quant_blockwise(const uint16_t* x, int64_t rows, int64_t cols,
                                   int64_t ld_q, float* scale, hipStream_t st) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (block_rows == 1 && block_cols == 128) {
-    hipLaunchKernelGGL(quant_1x128_kernel, dim3(unsigned((rows + 15) / 16)), dim3(256), 0, st, x, rows,
+    hipLaunchKernelGGL(quant_1x128_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, st, x, rows,
                        cols, ld_x, q, ld_q, scale);
   } else if (block_rows == 128 && block_cols == 128) {
     hipLaunchKernelGGL(quant_128x128_kernel, dim3(unsigned(cols / 128), unsigned(rows / 128)), dim3(256), 0,
