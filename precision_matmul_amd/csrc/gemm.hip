@@ -564,6 +564,10 @@ static int device_cus() {
 // which run closer to the streaming kernel's rate.
 template <Epi EPI, bool OUT_BF16, bool BIAS>
 hipError_t launch_tail(const GemmProblem& p, bool small, hipStream_t st) {
+  if (p.b_kn) {
+    if (small) return launch_cfg<128, 128, 2, 2, 3, EPI, true, OUT_BF16, BIAS, false>(p, st);
+    return launch_cfg<256, 128, 2, 2, 3, EPI, true, OUT_BF16, BIAS, false>(p, st);
+  }
   if (small) return launch_cfg<128, 128, 2, 2, 3, EPI, false, OUT_BF16, BIAS, false>(p, st);
   return launch_cfg<256, 128, 4, 2, 3, EPI, false, OUT_BF16, BIAS, false>(p, st);
 }
@@ -591,11 +595,11 @@ hipError_t launch_gemm_tail(const GemmProblem& p, bool small, hipStream_t st) {
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
   if (p.offsets) return launch_out<Epi::Row, false, true>(p, st);
   // The streaming kernel's grouped loads need leading dimensions of at least
-  // 128 bytes.  Its 256 x 256 tiles are handed out in rounds of one per CU;
+  // 128 bytes (256 for B stored [K, N]).  Its 256 x 256 tiles are handed out in rounds of one per CU;
   // when the last round would be less than half full, the streaming kernel
   // takes the rows of tiles that fill whole rounds and the rest of the rows
   // (the tail) run with 128 x 128 tiles, four times as many workgroups.
-  if (!p.b_kn && p.lda >= 128 && p.ldb >= 128) {
+  if (p.lda >= 128 && (p.b_kn ? p.ldb >= 256 : p.ldb >= 128)) {
     const int64_t tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     const int64_t tiles = tiles_m * tiles_n, cus = device_cus();
     const int64_t rem = tiles % cus;

@@ -60,7 +60,16 @@ constexpr int SY_FN = SY_TN / 16;
 
 __device__ __forceinline__ void sy_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-template <Epi EPI, bool OUT_BF16, bool BIAS, bool K_ALIGNED>
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// B stored [K, N]: LDS tile of 128 k-rows x 256 bytes; 16-byte chunk c of
+// row k at slot c ^ kswz(k).  The eight rows of one transposing read (k,
+// k + 1, .., k + 7 with the same 16-byte chunk) land in eight different
+// slots, and rows 16 apart (another lane group) in different slot sets.
+__device__ __forceinline__ int kswz(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
+__device__ __forceinline__ int kn_off(int k, int n) { return k * 256 + (((n >> 4) ^ kswz(k)) << 4) + (n & 15); }
+
+template <Epi EPI, bool OUT_BF16, bool BIAS, bool K_ALIGNED, bool B_KN>
 __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                                    int vec_out) {
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
@@ -98,7 +107,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   const int ch_even = (lane & 7) ^ (lane >> 4);
   const int ch_odd = (lane & 7) ^ (4 | (lane >> 4));
   const Rsrc rsA = make_rsrc4(p.A + row0 * p.lda, uint32_t(rows_valid) * uint32_t(p.lda));
-  const Rsrc rsB = make_rsrc4(p.B + n0 * p.ldb, uint32_t(cols_valid) * uint32_t(p.ldb));
+  [[maybe_unused]] const Rsrc rsB = make_rsrc4(p.B + n0 * p.ldb, uint32_t(cols_valid) * uint32_t(p.ldb));
   const uint32_t rowA = uint32_t(wave * 32 + ld_row) * uint32_t(p.lda);
   const uint32_t rowB = uint32_t(wave * 32 + ld_row) * uint32_t(p.ldb);
   const uint32_t stepA = 8u * uint32_t(p.lda) - 1024u;   // per-q change of the per-lane offset
@@ -107,7 +116,35 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
 
   // The group of A (or B) loads of K step kt into the stage at LDS address st;
   // steps past the end issue nothing.
+  // B stored [K, N]: the B tile is 128 k-rows of 256 bytes (n); 16-byte chunk
+  // c of row k sits at slot c ^ kswz(k).  Wave w fills rows [16 w, 16 w + 16):
+  // load q rows 16 w + 4 q + l / 16, lane l slot l % 16 (one 1 KiB block, at
+  // LDS block 4 w + q as for the [N, K] layout).  The per-step descriptor
+  // starts at row k0 of the tile's columns and ends with the matrix, so rows
+  // past K read zeros; columns past N read bytes of the next row (or zeros),
+  // which only reach output columns that are never stored.
+  [[maybe_unused]] const int kn_row = lane >> 4;
+  [[maybe_unused]] const int kn_slot = lane & 15;
+  auto load_group_kn = [&](int kt, uint32_t st) {
+    if (kt >= nk) return;
+    const int64_t k0 = int64_t(kt) * BK;
+    const int64_t rem = (p.K - k0) * p.ldb - n0;
+    const Rsrc r = make_rsrc4(p.B + k0 * p.ldb + n0, uint32_t(rem));
+    uint32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = wave * 16 + q * 4 + kn_row;
+      v[q] = uint32_t(row) * uint32_t(p.ldb) + uint32_t((kn_slot ^ kswz(row)) * 16) - uint32_t(q) * 1024u;
+    }
+    dma_b128x4(r, st + SY_A + wave * 4096, v[0], v[1], v[2], v[3], 0u);
+  };
   auto load_group = [&](bool is_b, int kt, uint32_t st) {
+    if constexpr (B_KN) {
+      if (is_b) {
+        load_group_kn(kt, st);
+        return;
+      }
+    }
     if (kt >= nk) return;
     const uint32_t k0 = uint32_t(kt) * BK;
     const uint32_t rowv = is_b ? rowB : rowA;
@@ -142,11 +179,19 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       sc_count = int64_t(nk) * p.N - n0 - (wave - 4) * 64;
       sc_stride = p.N;
     } else {
+      // 128x128: sB[n0/128 + wave - 4, kt] (grid [N/128, K/128] for B stored
+      // [N, K], [K/128, N/128] for B stored [K, N])
       const int64_t nb = n0 / 128 + (wave - 4);
       const bool in = wave < 6 && nb < p.N / 128;
-      sc_base = p.sb + (in ? nb * nk : 0);
-      sc_count = in ? nk : 0;
-      sc_stride = 1;
+      if constexpr (B_KN) {
+        sc_base = p.sb + (in ? nb : 0);
+        sc_count = in ? int64_t(nk) * (p.N / 128) - nb : 0;
+        sc_stride = p.N / 128;
+      } else {
+        sc_base = p.sb + (in ? nb * nk : 0);
+        sc_count = in ? nk : 0;
+        sc_stride = 1;
+      }
     }
   }
   [[maybe_unused]] auto load_scales = [&](int kt, uint32_t st) {
@@ -174,6 +219,30 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     const v4i lo = *reinterpret_cast<const v4i*>(tile + lds_off(r, fq));
     const v4i hi = *reinterpret_cast<const v4i*>(tile + lds_off(r, fq + 4));
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  // B stored [K, N]: the 16 x 128 fragment of columns [n0, n0 + 16) from four
+  // transposing reads.  In each 16-lane group, lane 2 j + h points at the 8
+  // bytes of row kb + j, columns n0 + 8 h .. +8; the read hands lane i the
+  // bytes of column n0 + i in rows kb .. kb + 7 (lanes 0..7 from the even
+  // lanes' rows, 8..15 from the odd lanes').  The four reads give lane l
+  // (group q = l / 16) rows 16 q .. 16 q + 15 and 64 + 16 q .. +15: the same
+  // chunks q and q + 4 that read_frag takes from an [N, K] tile.
+  // The four rows of a lane differ by multiples of 8 in bits 3 and 6 only, so
+  // they share kswz and sit at fixed distances; with nc a multiple of 16
+  // below 256 the offset of (k, nc + 8 h) is kn_off(k, 8 h) ^ nc.
+  [[maybe_unused]] const int kn_base = kn_off(fq * 16 + (frow >> 1), (frow & 1) * 8);
+  [[maybe_unused]] auto read_frag_kn = [&](const uint8_t* tile, int nc) {
+    const uint8_t* b = tile + (kn_base ^ nc);
+    v2i r[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      r[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i*)(b + ((t >> 1) * 64 + (t & 1) * 8) * 256));
+    return v8i{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+  };
+  auto read_b = [&](const uint8_t* tile, int nc) {
+    if constexpr (B_KN) return read_frag_kn(tile, nc);
+    else return read_frag(tile, nc + frow);
   };
   auto stage_ptr = [&](int s) -> const uint8_t* { return s == 0 ? stage0 : stage1; };
   // Blockwise: per-lane scales of the 4 row fragments (sA of the lane's 4
@@ -255,9 +324,9 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
         // B fragment of the next column (column 7: column 0 of the next step)
         if (i == 0) {
           if (j + 1 < SY_FN) {
-            bring[(j + 1) & 1] = read_frag(Bs, col_base + (j + 1) * 16 + frow);
+            bring[(j + 1) & 1] = read_b(Bs, col_base + (j + 1) * 16);
           } else {
-            bring[0] = read_frag(An + SY_A, col_base + frow);
+            bring[0] = read_b(An + SY_A, col_base);
           }
         }
         // next step's A fragment i, right after its last use
@@ -289,7 +358,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < SY_FM; ++i) a[i] = read_frag(stage0, row_base + i * 16 + frow);
-    bring[0] = read_frag(stage0 + SY_A, col_base + frow);
+    bring[0] = read_b(stage0 + SY_A, col_base);
     if constexpr (BLOCKWISE) read_fa(stage0, fa[0], sbv[0]);
     load_group(false, 1, lds1);
     for (int kt = 0; kt < nk; kt += 2) {
@@ -380,7 +449,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   }
 }
 
-template <Epi EPI, bool OUT_BF16, bool BIAS>
+template <Epi EPI, bool OUT_BF16, bool BIAS, bool B_KN>
 hipError_t launch_sym(const GemmProblem& p, hipStream_t st) {
   const int tiles_m = int((p.row_end - p.row_begin + SY_BM - 1) / SY_BM);
   const int tiles_n = int((p.N + SY_BN - 1) / SY_BN);
@@ -391,10 +460,10 @@ hipError_t launch_sym(const GemmProblem& p, hipStream_t st) {
   const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
   if (BLOCKWISE || p.K % BK == 0)
-    hipLaunchKernelGGL((gemm_sym_kernel<EPI, OUT_BF16, BIAS, true>), dim3(grid), dim3(SY_NW * 64), 0, st, p, tiles_m,
+    hipLaunchKernelGGL((gemm_sym_kernel<EPI, OUT_BF16, BIAS, true, B_KN>), dim3(grid), dim3(SY_NW * 64), 0, st, p, tiles_m,
                        tiles_n, vec_out);
   else if constexpr (!BLOCKWISE)
-    hipLaunchKernelGGL((gemm_sym_kernel<EPI, OUT_BF16, BIAS, false>), dim3(grid), dim3(SY_NW * 64), 0, st, p, tiles_m,
+    hipLaunchKernelGGL((gemm_sym_kernel<EPI, OUT_BF16, BIAS, false, B_KN>), dim3(grid), dim3(SY_NW * 64), 0, st, p, tiles_m,
                        tiles_n, vec_out);
   return hipGetLastError();
 }
@@ -402,13 +471,17 @@ hipError_t launch_sym(const GemmProblem& p, hipStream_t st) {
 template <Epi EPI>
 hipError_t launch_sym_out(const GemmProblem& p, hipStream_t st) {
   const bool bias = p.bias != nullptr;
-  if (p.out_bf16) return bias ? launch_sym<EPI, true, true>(p, st) : launch_sym<EPI, true, false>(p, st);
-  return bias ? launch_sym<EPI, false, true>(p, st) : launch_sym<EPI, false, false>(p, st);
+  if (p.b_kn) {
+    if (p.out_bf16) return bias ? launch_sym<EPI, true, true, true>(p, st) : launch_sym<EPI, true, false, true>(p, st);
+    return bias ? launch_sym<EPI, false, true, true>(p, st) : launch_sym<EPI, false, false, true>(p, st);
+  }
+  if (p.out_bf16) return bias ? launch_sym<EPI, true, true, false>(p, st) : launch_sym<EPI, true, false, false>(p, st);
+  return bias ? launch_sym<EPI, false, true, false>(p, st) : launch_sym<EPI, false, false, false>(p, st);
 }
 
 }  // namespace
 
-// Plain (non-grouped) GEMM with B stored [N, K], streaming schedule.
+// Plain (non-grouped) GEMM, streaming schedule (B stored [N, K] or [K, N]).
 hipError_t launch_gemm_streaming(const GemmProblem& p, hipStream_t st) {
   switch (p.epi) {
     case Epi::Tensor: return launch_sym_out<Epi::Tensor>(p, st);

@@ -146,10 +146,24 @@ def test_blockwise_grad_weight(T, N_out, K_in):
 # gives 20 x 16 tiles and a 64-tile tail (256 x 128 tail tiles); elsewhere
 # the same shapes still check the full result.
 @pytest.mark.parametrize("M", [4400, 5008])
-@pytest.mark.parametrize("recipe", ["tensorwise", "rowwise", "blockwise", "grad_weight"])
+@pytest.mark.parametrize("recipe", ["tensorwise", "rowwise", "blockwise", "grad_weight", "grad_input",
+                                    "tensorwise_kn"])
 def test_split_tail_rows(recipe, M):
     N, K = 4096, 256
-    if recipe == "grad_weight":
+    if recipe == "grad_input":
+        # B stored [K, N]: grad_output [M, 256] @ weight [256, 4096]
+        inp = workloads.blockwise(M=M, N=K, K=N, seed=81)
+        qg, sg, rg, rsg = _quant_both(inp["grad_output"], "1x128")
+        qw, sw, rw, rsw = _quant_both(inp["weight"], "128x128")
+        out = fp8mm.fp8_linear_grad_input(qg, sg, "1x128", qw, sw, "128x128")
+        ref = gemm.linear_grad_input(rg, rsg, "1x128", rw, rsw, "128x128", out_dtype=None)
+    elif recipe == "tensorwise_kn":
+        inp = workloads.tensorwise(n=N, m=M, k=K, seed=82)
+        qa, sa, ra, rsa = _quant_both(inp["A"], "tensorwise")
+        qb, sb, rb, rsb = _quant_both(np.ascontiguousarray(inp["B"].T), "tensorwise")   # [K, N]
+        out = fp8mm.fp8_scaled_mm(qa, qb, sa, "tensorwise", sb, "tensorwise", b_layout="KN")
+        ref = gemm.scaled_mm(ra, rb, rsa, "tensorwise", rsb, "tensorwise", layout="KN", out_dtype=None)
+    elif recipe == "grad_weight":
         inp = workloads.grad_weight(T=K, N_out=M, K_in=N, seed=77)
         qg, sg, rg, rsg = _quant_both(inp["grad_output"], "128x1", transpose_out=True)
         qx, sx, rx, rsx = _quant_both(inp["input"], "128x1", transpose_out=True)
