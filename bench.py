@@ -218,25 +218,37 @@ def cpu_baseline(workloads):
                       f"({2.0 * Ms * N * K / 1e9:.0f} GFLOP), rounding to bf16"}
 
 
-def measured_traffic(workload):
-    """HBM bytes per GEMM launch from the committed counter summary
-    profiles/<workload>.md (FETCH_SIZE + WRITE_SIZE, each scaled by what the
-    counter reads for a plain copy of known size).  None when there is no
-    summary, or when the GEMM source has changed since the counters were taken
-    (the summary records the sha256 of gemm.hip it was measured with)."""
+GEMM_SOURCES = ("gemm.hip", "gemm_sym.hip", "gemm_common.hpp", "launch.hpp")
+
+
+def gemm_source_sha():
+    """sha256 over the GEMM kernel sources, in GEMM_SOURCES order."""
     import hashlib
 
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, "precision_matmul_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_profile(workload):
+    """Counter figures of one GEMM call from the committed summary
+    profiles/<workload>.md: HBM bytes (FETCH_SIZE + WRITE_SIZE summed over the
+    call's launches, each scaled by what the counter reads for a plain copy of
+    known size) and the kernels the call launches.  Traffic is None when there
+    is no summary, or when the GEMM sources have changed since the counters
+    were taken (the summary records their sha256)."""
     path = os.path.join(ROOT, "profiles", workload + ".md")
-    src = os.path.join(ROOT, "precision_matmul_amd", "csrc", "gemm.hip")
     try:
         text = open(path).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = gemm_source_sha()
     except OSError:
-        return None
-    got = dict(re.findall(r"^(traffic_bytes_per_launch|kernel_source_sha256): *(\S+)$", text, re.M))
-    if got.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in got:
-        return None
-    return int(got["traffic_bytes_per_launch"])
+        return None, None
+    got = dict(re.findall(r"^(traffic_bytes_per_call|gemm_sources_sha256|gemm_call_kernels): *(.+)$", text, re.M))
+    kernels = got.get("gemm_call_kernels")
+    if got.get("gemm_sources_sha256", "").strip() != sha or "traffic_bytes_per_call" not in got:
+        return None, kernels
+    return int(got["traffic_bytes_per_call"]), kernels
 
 
 def main():
@@ -296,7 +308,7 @@ def main():
     print(f"[bench] step {ms_step:.3f} ms, gemm {gemm_ms:.3f} ms ({achieved:.1f} TFLOP/s)", file=sys.stderr,
           flush=True)
 
-    traffic = measured_traffic(args.workload)
+    traffic, call_kernels = measured_profile(args.workload)
 
     result = {
         "metric": "FP8 scaled-GEMM TFLOP/s at 1 MI355X + % of FP8 MFMA peak, per recipe",
@@ -313,7 +325,7 @@ def main():
         "data": "synthetic (seeded bf16 normals, shapes of the method's benchmarks)",
         "config": {"workload": args.workload, "recipe": wl["recipe"], "shape_MNK": list(wl["shape"]),
                    "step": "quantize both operands + scaled GEMM, bf16 out", "out_dtype": "bf16"},
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (" + wl["recipe"] + ")",
+        "roofline": {"bound": "mfma", "kernel": "GEMM call, " + wl["recipe"] + ": " + (call_kernels or "see profile"),
                      "achieved": round(achieved, 2), "peak": FP8_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / FP8_DENSE_PEAK_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_bytes": wl["gemm_bytes"], "gemm_ms": round(gemm_ms, 4)},
