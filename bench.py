@@ -191,12 +191,12 @@ def time_kernel(torch, fn, iters, warmup=3):
 
 def cpu_baseline(workloads):
     """The oracle (untuned numpy + OpenBLAS float64) on a bounded sample of the
-    default workload: rows [0, 2080) of the 16640x5120x8192 blockwise forward
+    default workload: rows [0, 12480) of the 16640x5120x8192 blockwise forward
     step (quantize those input rows and the full weight, then the GEMM)."""
     from oracle import gemm as ogemm
     from oracle import quant as oquant
 
-    Ms, N, K = 2080, 5120, 8192
+    Ms, N, K = 12480, 5120, 8192
     inp = workloads.blockwise(M=16640, N=N, K=K)
     x = inp["input"][:Ms]
     w = inp["weight"]

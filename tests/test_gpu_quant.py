@@ -121,6 +121,50 @@ def test_blockwise_specials():
         _check(q, s, rq, rs, f"specials {block}")
 
 
+def _every_bf16_under(amax_bits):
+    """A [128, 4096] bf16 block whose every row, 128-column group, 128-row
+    column group and 128x128 block has amax exactly bf16(amax_bits): row 0 and
+    column 0 of each 128-column group hold the amax, and the other slots hold
+    every finite bf16 pattern of magnitude <= amax (both signs), cycled."""
+    amax = quant.bf16_to_f32(np.array([amax_bits], np.uint16))[0]
+    pats = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    mag = quant.bf16_to_f32(pats)
+    pats = pats[np.isfinite(mag) & (np.abs(mag) <= amax)]
+    x = np.full((128, 4096), amax_bits, np.uint16)
+    slots = np.ones((128, 4096), bool)
+    slots[0, :] = False
+    slots[:, ::128] = False
+    n = int(slots.sum())
+    assert pats.size <= n
+    x[slots] = np.resize(pats, n)
+    return x
+
+
+def test_every_bf16_value_at_several_scales():
+    """Exhaustive over the bf16 inputs: for each amax (scale amax/448 exactly
+    1, a power of two, an awkward ratio, large, tiny and below 2^-90), every
+    bf16 value that the amax admits goes through each quantizer's cast and
+    must give the oracle's code."""
+    amaxes = [448.0, 1.0, 3.140625, 61440.0, 2.0 ** -20, 1e-30]
+    bits = workloads.f32_to_bf16_bits(np.array(amaxes, np.float32))
+    blocks = [_every_bf16_under(int(b)) for b in bits]
+    for b, blk in zip(amaxes, blocks):
+        say(f"tensorwise every bf16 under {b}")
+        q, s = fp8mm.fp8_quantize_tensorwise(bf16_dev(blk))
+        rq, rs = quant.quantize_tensorwise(blk)
+        _check(q, s, rq, rs, f"tensorwise every bf16 under {b}")
+    x = np.concatenate(blocks)
+    say("rowwise / blockwise every bf16")
+    q, s = fp8mm.fp8_quantize_rowwise(bf16_dev(x), eps=0.0)
+    rq, rs = quant.quantize_rowwise(x, eps=0.0)
+    _check(q, s, rq, rs, "rowwise every bf16")
+    for block in ((1, 128), (128, 128), (128, 1)):
+        for transpose in ([False, True] if block == (128, 1) else [False]):
+            q, s = fp8mm.fp8_quantize_blockwise(bf16_dev(x), block, transpose_out=transpose)
+            rq, rs = quant.quantize_blockwise(x, *block, transpose_out=transpose)
+            _check(q, s, rq, rs, f"every bf16 {block} T={transpose}")
+
+
 def test_quantize_is_deterministic_across_runs():
     x = workloads.blockwise(M=512, N=128, K=2048)["input"]
     xd = bf16_dev(x)
