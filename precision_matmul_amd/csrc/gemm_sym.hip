@@ -66,6 +66,9 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 // row k at slot c ^ kswz(k).  The eight rows of one transposing read (k,
 // k + 1, .., k + 7 with the same 16-byte chunk) land in eight different
 // slots, and rows 16 apart (another lane group) in different slot sets.
+__device__ __forceinline__ float fac(float f, int) { return f; }
+__device__ __forceinline__ float fac(const v4f& f, int e) { return f[e]; }
+
 __device__ __forceinline__ int kswz(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
 __device__ __forceinline__ int kn_off(int k, int n) { return k * 256 + (((n >> 4) ^ kswz(k)) << 4) + (n & 15); }
 
@@ -73,6 +76,13 @@ template <Epi EPI, bool OUT_BF16, bool BIAS, bool K_ALIGNED, bool B_KN>
 __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                                    int vec_out) {
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
+  // Operand order of the MFMA.  SWAP computes each 16 x 16 output block
+  // transposed (B fragment as the instruction's first operand), so a lane
+  // holds one output row and four adjacent columns: one promotion factor per
+  // lane and row fragment for a 128x128 B.  A 128x1 B scales columns, so it
+  // keeps the plain order (one output column and four rows per lane).
+  constexpr bool SWAP = EPI != Epi::Block128x1;
+  using Fac = std::conditional_t<SWAP, float, v4f>;
   constexpr int OUTB = OUT_BF16 ? 2 : 4;
   constexpr int EPI_PASSES = epi_passes(SY_NW, SY_TM, SY_TN, OUTB, SY_STAGE);
   constexpr int EPI_COLS = SY_TN / EPI_PASSES;
@@ -248,11 +258,14 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   // Blockwise: per-lane scales of the 4 row fragments (sA of the lane's 4
   // rows) and the B scales (128x128: the block scale, folded into the row
   // factors in column 0 of the step that uses them; 128x1: one per column).
-  auto read_fa = [&](const uint8_t* st, v4f* fa_out, float* sbv_out) {
+  auto read_fa = [&](const uint8_t* st, Fac* fa_out, float* sbv_out) {
     const float* sas = reinterpret_cast<const float*>(st + SY_A + SY_B);
     const float* sbs = sas + SY_SCALE / 4;
 #pragma unroll
-    for (int i = 0; i < SY_FM; ++i) fa_out[i] = *reinterpret_cast<const v4f*>(sas + row_base + i * 16 + fq * 4);
+    for (int i = 0; i < SY_FM; ++i) {
+      if constexpr (SWAP) fa_out[i] = sas[row_base + i * 16 + frow];
+      else fa_out[i] = *reinterpret_cast<const v4f*>(sas + row_base + i * 16 + fq * 4);
+    }
     if constexpr (EPI == Epi::Block128x128) {
       sbv_out[0] = sbs[(col_base / 128) * 64];
     } else if constexpr (EPI == Epi::Block128x1) {
@@ -263,11 +276,11 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
 
   v8i a[SY_FM];
   v8i bring[2];
-  [[maybe_unused]] v4f fa[2][SY_FM];           // promotion factors of the current / next step
+  [[maybe_unused]] Fac fa[2][SY_FM];           // promotion factors of the current / next step
   [[maybe_unused]] float sbv[2][SY_FN];
   // Blockwise promotion runs two MFMAs behind: pending results and where they go.
   [[maybe_unused]] v4f pend_t[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-  [[maybe_unused]] v4f pend_f[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+  [[maybe_unused]] Fac pend_f[2] = {Fac{}, Fac{}};
 
   // ---------------- one K step ----------------
   // F selects the promotion-factor buffer of this step (steps alternate).
@@ -294,23 +307,24 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
         const int m = j * SY_FM + i;     // slot in the step
         const v8i& bf = bring[j & 1];
         if constexpr (!BLOCKWISE) {
-          acc[i][j] = mfma_16x16x128(a[i], bf, acc[i][j]);
+          acc[i][j] = SWAP ? mfma_16x16x128(bf, a[i], acc[i][j]) : mfma_16x16x128(a[i], bf, acc[i][j]);
         } else {
-          const v4f t = mfma_16x16x128(a[i], bf, v4f{0.f, 0.f, 0.f, 0.f});
+          const v4f t = SWAP ? mfma_16x16x128(bf, a[i], v4f{0.f, 0.f, 0.f, 0.f})
+                             : mfma_16x16x128(a[i], bf, v4f{0.f, 0.f, 0.f, 0.f});
           // promote the result of slot m - 2 (possibly of the previous step)
           {
             const int mp = m - 2;
             const int ip = (mp + 32) % 32 % SY_FM;
             const int jp = (mp + 32) % 32 / SY_FM;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[ip][jp][e] = __builtin_fmaf(pend_t[m & 1][e], pend_f[m & 1][e], acc[ip][jp][e]);
+            for (int e = 0; e < 4; ++e) acc[ip][jp][e] = __builtin_fmaf(pend_t[m & 1][e], fac(pend_f[m & 1], e), acc[ip][jp][e]);
             asm volatile("" ::"v"(acc[ip][jp]));
           }
           pend_t[m & 1] = t;
           if constexpr (EPI == Epi::Block128x128) {
             if (j == 0) fa[F][i] = fa[F][i] * sbv[F][0];
             pend_f[m & 1] = fa[F][i];
-          } else {
+          } else if constexpr (!SWAP) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) pend_f[m & 1][e] = fa[F][i][e] * sbv[F][j];
           }
@@ -371,7 +385,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       for (int mm = 30; mm < 32; ++mm) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[mm % SY_FM][mm / SY_FM][e] = __builtin_fmaf(pend_t[mm & 1][e], pend_f[mm & 1][e], acc[mm % SY_FM][mm / SY_FM][e]);
+          acc[mm % SY_FM][mm / SY_FM][e] = __builtin_fmaf(pend_t[mm & 1][e], fac(pend_f[mm & 1], e), acc[mm % SY_FM][mm / SY_FM][e]);
       }
     }
   }
@@ -382,14 +396,16 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   uint8_t* ep = (wave < SY_NW / 2 ? stage0 : stage1) + (wave % (SY_NW / 2)) * SY_TM * EPI_PITCH;
   [[maybe_unused]] float s_tensor = 0.f;
   if constexpr (EPI == Epi::Tensor) s_tensor = p.sa[0] * p.sb[0];
+  // Row scales of the lane's rows: SWAP, one row per row fragment (i * 16 +
+  // frow); otherwise four (i * 16 + 4 fq + e).
   [[maybe_unused]] float sar[SY_FM][4];
   if constexpr (EPI == Epi::Row) {
 #pragma unroll
     for (int i = 0; i < SY_FM; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int rt = row_base + i * 16 + fq * 4 + e;
-        sar[i][e] = rt < rows_valid ? p.sa[row0 + rt] : 0.f;
+        const int rt = row_base + i * 16 + (SWAP ? frow : fq * 4 + e);
+        sar[i][e] = (SWAP && e > 0) ? sar[i][0] : (rt < rows_valid ? p.sa[row0 + rt] : 0.f);
       }
   }
 #pragma unroll
@@ -398,26 +414,46 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
 #pragma unroll
     for (int jj = 0; jj < FNP; ++jj) {
       const int j = pass * FNP + jj;
-      const int cl = jj * 16 + frow;
-      const int ct = col_base + j * 16 + frow;
-      const bool cin = ct < cols_valid;
-      [[maybe_unused]] float sbc = 0.f;
-      if constexpr (EPI == Epi::Row) sbc = cin ? p.sb[n0 + ct] : 0.f;
-      float bias_v = 0.f;
-      if constexpr (BIAS) bias_v = cin ? __uint_as_float(uint32_t(p.bias[n0 + ct]) << 16) : 0.f;
+      // output columns of the lane's values: SWAP, four adjacent (e);
+      // otherwise one
+      float sbc[4] = {0.f, 0.f, 0.f, 0.f};
+      float bias_v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < (SWAP ? 4 : 1); ++e) {
+        const int ct = col_base + j * 16 + (SWAP ? fq * 4 + e : frow);
+        const bool cin = ct < cols_valid;
+        if constexpr (EPI == Epi::Row) sbc[e] = cin ? p.sb[n0 + ct] : 0.f;
+        if constexpr (BIAS) bias_v[e] = cin ? __uint_as_float(uint32_t(p.bias[n0 + ct]) << 16) : 0.f;
+      }
 #pragma unroll
       for (int i = 0; i < SY_FM; ++i) {
+        float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float v = acc[i][j][e];
-          if constexpr (EPI == Epi::Tensor) v = v * s_tensor;
-          if constexpr (EPI == Epi::Row) v = (v * sar[i][e]) * sbc;
-          if constexpr (BIAS) v = v + bias_v;
-          uint8_t* dst = ep + (i * 16 + fq * 4 + e) * EPI_PITCH + cl * OUTB;
-          if constexpr (OUT_BF16)
-            *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_rne(v);
-          else
-            *reinterpret_cast<float*>(dst) = v;
+          const int ce = SWAP ? e : 0;
+          v[e] = acc[i][j][e];
+          if constexpr (EPI == Epi::Tensor) v[e] = v[e] * s_tensor;
+          if constexpr (EPI == Epi::Row) v[e] = (v[e] * sar[i][e]) * sbc[ce];
+          if constexpr (BIAS) v[e] = v[e] + bias_v[ce];
+        }
+        if constexpr (SWAP) {
+          uint8_t* dst = ep + (i * 16 + frow) * EPI_PITCH + (jj * 16 + fq * 4) * OUTB;
+          if constexpr (OUT_BF16) {
+            const uint32_t lo = uint32_t(f32_to_bf16_rne(v[0])) | (uint32_t(f32_to_bf16_rne(v[1])) << 16);
+            const uint32_t hi = uint32_t(f32_to_bf16_rne(v[2])) | (uint32_t(f32_to_bf16_rne(v[3])) << 16);
+            *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+          } else {
+            *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint8_t* dst = ep + (i * 16 + fq * 4 + e) * EPI_PITCH + (jj * 16 + frow) * OUTB;
+            if constexpr (OUT_BF16)
+              *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_rne(v[e]);
+            else
+              *reinterpret_cast<float*>(dst) = v[e];
+          }
         }
       }
     }
