@@ -40,6 +40,10 @@
 
 #include "gemm_common.hpp"
 
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
 namespace fp8mm {
 namespace {
 
@@ -175,6 +179,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
 
   const int K = int(p.K);
   const int nk = (K + BK - 1) / BK;
+  // Split K: grid row y covers K steps [kt_begin, kt_end) (all of K when the
+  // grid has one row).
+  const int kt_begin = int(int64_t(nk) * blockIdx.y / gridDim.y);
+  const int kt_end = int(int64_t(nk) * (blockIdx.y + 1) / gridDim.y);
 
   // ---------------- loaders ----------------
   // Direct-to-LDS: load number q < LA of wave w fills tile rows
@@ -300,16 +308,19 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
   const int row_base = wm * TM;
   const int col_base = wn * TN;
   const int frow = lane & 15;   // fragment row (A) / column (B) of this lane
-  const int fq = lane >> 4;     // which 32-byte quarter of the 128-byte K block
+  const int fq = lane >> 4;     // the lane's 16-byte chunks of the 128-byte K block: fq and fq + 4
   v4f acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // Both operands take the same k order, so the contraction is unchanged;
+  // chunks q and q + 4 (rather than 2q, 2q + 1) keep the 16-lane groups of
+  // one read on distinct LDS banks.
   auto read_frag = [&](const uint8_t* tile, int r) {
-    const v4i lo = *reinterpret_cast<const v4i*>(tile + lds_off(r, 2 * fq));
-    const v4i hi = *reinterpret_cast<const v4i*>(tile + lds_off(r, 2 * fq + 1));
+    const v4i lo = *reinterpret_cast<const v4i*>(tile + lds_off(r, fq));
+    const v4i hi = *reinterpret_cast<const v4i*>(tile + lds_off(r, fq + 4));
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
 
@@ -400,24 +411,25 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
     // this stage and its LDS reads / writes, so after the barrier the stage is
     // complete and the stage refilled next is no longer being read.
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((D - 1) * LPS) : "memory");
-    const bool live = kt + D < nk;
+    const bool live = kt + D < kt_end;
     kn_load(kt + D, live);
     compute(stage_c, kt, live);
     kn_store((S + D) % STAGES);
   };
-  if (nk > 0) {
+  if (kt_end > kt_begin) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
+      const int kd = kt_begin + d;
 #pragma unroll
-      for (int q = 0; q < LDIRECT; ++q) issue_one(q, d, d, d < nk);
-      kn_load(d, d < nk);
+      for (int q = 0; q < LDIRECT; ++q) issue_one(q, d, kd, kd < kt_end);
+      kn_load(kd, kd < kt_end);
       kn_store(d);
     }
-    for (int kt = 0; kt < nk; kt += STAGES) {
+    for (int kt = kt_begin; kt < kt_end; kt += STAGES) {
       step(std::integral_constant<int, 0>{}, kt);
-      if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+      if (kt + 1 < kt_end) step(std::integral_constant<int, 1>{}, kt + 1);
       if constexpr (STAGES > 2) {
-        if (kt + 2 < nk) step(std::integral_constant<int, 2 % STAGES>{}, kt + 2);
+        if (kt + 2 < kt_end) step(std::integral_constant<int, 2 % STAGES>{}, kt + 2);
       }
     }
   }
@@ -480,7 +492,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
       const int ct = col_base + pass * EPI_COLS + ch * EPR;
       if (rt >= ti.rows_valid || ct >= ti.cols_valid) continue;
       const uint8_t* src = ep + rl * EPI_PITCH + ch * 16;
-      uint8_t* dst = reinterpret_cast<uint8_t*>(p.out) + ((ti.row0 + rt) * p.ldo + ti.n0 + ct) * OUTB;
+      uint8_t* dst = reinterpret_cast<uint8_t*>(p.out) +
+                     ((int64_t(blockIdx.y) * p.split_stride + (ti.row0 - p.out_row0 + rt) * p.ldo + ti.n0 + ct) * OUTB);
       if (vec_out && ct + EPR <= ti.cols_valid) {
         *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
       } else {
@@ -511,11 +524,11 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
   const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
   if (BLOCKWISE || p.K % BK == 0)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, EPI, B_KN, OUT_BF16, BIAS, GROUPED, true>), dim3(grid),
-                       dim3(WM * WN * 64), 0, st, p, tiles_m, tiles_n, vec_out);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, EPI, B_KN, OUT_BF16, BIAS, GROUPED, true>),
+                       dim3(grid, max(1, p.splits)), dim3(WM * WN * 64), 0, st, p, tiles_m, tiles_n, vec_out);
   else if constexpr (!BLOCKWISE)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, EPI, B_KN, OUT_BF16, BIAS, GROUPED, false>), dim3(grid),
-                       dim3(WM * WN * 64), 0, st, p, tiles_m, tiles_n, vec_out);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, EPI, B_KN, OUT_BF16, BIAS, GROUPED, false>),
+                       dim3(grid, max(1, p.splits)), dim3(WM * WN * 64), 0, st, p, tiles_m, tiles_n, vec_out);
   return hipGetLastError();
 }
 
@@ -558,10 +571,10 @@ static int device_cus() {
   return cache[dev];
 }
 
-// The tail rows of a plain [N, K] GEMM.  A short tail (its 128 x 128 tiles
-// fit in half the compute units) uses 128 x 128 tiles on 4 waves, four
-// workgroups per 256 x 256 tile; a longer one 256 x 128 tiles on 8 waves,
-// which run closer to the streaming kernel's rate.
+// The tail rows of a plain GEMM.  A short tail (its 128 x 128 tiles fit in
+// half the compute units) uses 128 x 128 tiles on 4 waves, four workgroups
+// per 256 x 256 tile; a longer one 256 x 128 tiles on 8 waves (B stored
+// [K, N]: 4 waves), which run closer to the streaming kernel's rate.
 template <Epi EPI, bool OUT_BF16, bool BIAS>
 hipError_t launch_tail(const GemmProblem& p, bool small, hipStream_t st) {
   if (p.b_kn) {
@@ -590,6 +603,132 @@ hipError_t launch_gemm_tail(const GemmProblem& p, bool small, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// Sum of the split-K partials: out[row_begin + r, c] = round(sum_y part[y][r][c]
+// (+ bias[c])), the slices added in order y = 0, 1, ...  One thread per four
+// adjacent columns of one row.
+template <bool OUT_BF16, bool BIAS>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int splits, int64_t slice,
+                                                            int64_t rows, int64_t N, const uint16_t* bias,
+                                                            void* out, int64_t ldo, int64_t row_begin) {
+  const int64_t n4 = (N + 3) / 4;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= rows * n4) return;
+  const int64_t r = idx / n4;
+  const int64_t c = (idx % n4) * 4;
+  const int nc = int(min<int64_t>(4, N - c));
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int y = 0; y < splits; ++y) {
+    const float* src = part + y * slice + r * N + c;
+    if (nc == 4 && (N & 3) == 0) {
+      const v4f t = *reinterpret_cast<const v4f*>(src);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += t[e];
+    } else {
+      for (int e = 0; e < nc; ++e) v[e] += src[e];
+    }
+  }
+  if constexpr (BIAS) {
+    for (int e = 0; e < nc; ++e) v[e] += __uint_as_float(uint32_t(bias[c + e]) << 16);
+  }
+  const int64_t o = (row_begin + r) * ldo + c;
+  if constexpr (OUT_BF16) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(out) + o;
+    for (int e = 0; e < nc; ++e) dst[e] = f32_to_bf16_rne(v[e]);
+  } else {
+    float* dst = reinterpret_cast<float*>(out) + o;
+    for (int e = 0; e < nc; ++e) dst[e] = v[e];
+  }
+}
+
+// Split-K workspace: one device buffer per (device, stream), allocated on
+// first use and grown when a call needs more.  Calls on one stream use it in
+// stream order; calls on different streams use different buffers.
+hipError_t workspace_get(void** ptr, size_t bytes, hipStream_t st) {
+  struct Entry {
+    int dev;
+    hipStream_t st;
+    void* ptr;
+    size_t bytes;
+  };
+  static std::vector<Entry> cache;
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  Entry* w = nullptr;
+  for (Entry& c : cache)
+    if (c.dev == dev && c.st == st) w = &c;
+  if (!w) {
+    cache.push_back(Entry{dev, st, nullptr, 0});
+    w = &cache.back();
+  }
+  if (w->bytes < bytes) {
+    if (w->ptr) {
+      // earlier calls on this stream may still use the old buffer
+      e = hipStreamSynchronize(st);
+      if (e != hipSuccess) return e;
+      (void)hipFree(w->ptr);
+      w->ptr = nullptr;
+      w->bytes = 0;
+    }
+    e = hipMalloc(&w->ptr, bytes);
+    if (e != hipSuccess) {
+      w->ptr = nullptr;
+      return e;
+    }
+    w->bytes = bytes;
+  }
+  *ptr = w->ptr;
+  return hipSuccess;
+}
+
+// The short tail split along K: 128 x 128 tiles x `splits` K ranges, fp32
+// partials in a workspace, then one pass that sums them, adds the bias and
+// rounds once.  Returns hipErrorNotSupported (nothing launched) when no
+// workspace can be had; the caller then runs the unsplit tail.  A tail needs
+// splits x rows x N x 4 bytes (15.7 MB for 256 rows x 5120 x 3 splits).
+hipError_t launch_tail_splitk(const GemmProblem& p, int splits, hipStream_t st) {
+  const int64_t rows = p.row_end - p.row_begin;
+  const int64_t slice = rows * p.N;
+  void* ws = nullptr;
+  if (workspace_get(&ws, size_t(splits) * size_t(slice) * sizeof(float), st) != hipSuccess) {
+    (void)hipGetLastError();
+    return hipErrorNotSupported;
+  }
+  GemmProblem q = p;
+  q.out = ws;
+  q.ldo = p.N;
+  q.out_bf16 = false;
+  q.bias = nullptr;
+  q.out_row0 = p.row_begin;
+  q.split_stride = slice;
+  q.splits = splits;
+  hipError_t e = launch_gemm_tail(q, true, st);
+  if (e == hipSuccess) {
+    const int64_t threads = rows * ((p.N + 3) / 4);
+    const dim3 grid(unsigned((threads + 255) / 256));
+    const float* part = static_cast<const float*>(ws);
+    if (p.out_bf16) {
+      if (p.bias)
+        hipLaunchKernelGGL((splitk_reduce_kernel<true, true>), grid, dim3(256), 0, st, part, splits, slice, rows, p.N,
+                           p.bias, p.out, p.ldo, p.row_begin);
+      else
+        hipLaunchKernelGGL((splitk_reduce_kernel<true, false>), grid, dim3(256), 0, st, part, splits, slice, rows,
+                           p.N, p.bias, p.out, p.ldo, p.row_begin);
+    } else {
+      if (p.bias)
+        hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), grid, dim3(256), 0, st, part, splits, slice, rows,
+                           p.N, p.bias, p.out, p.ldo, p.row_begin);
+      else
+        hipLaunchKernelGGL((splitk_reduce_kernel<false, false>), grid, dim3(256), 0, st, part, splits, slice, rows,
+                           p.N, p.bias, p.out, p.ldo, p.row_begin);
+    }
+    e = hipGetLastError();
+  }
+  return e;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
@@ -611,7 +750,17 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
     const hipError_t e = launch_gemm_streaming(head, st);
     if (e != hipSuccess) return e;
     const int64_t tail_tiles = (tiles_m - tm_main) * tiles_n;
-    return launch_gemm_tail(tail, 4 * tail_tiles <= cus / 2, st);
+    const bool small = 4 * tail_tiles <= cus / 2;
+    // A short tail leaves most compute units idle: split its K range so the
+    // 128 x 128 tiles times the splits cover the device, each split keeping at
+    // least 8 K steps.
+    const int64_t nk = (p.K + 127) / 128;
+    const int64_t splits = small ? std::min<int64_t>({cus / (4 * tail_tiles), nk / 8, 8}) : 1;
+    if (splits >= 2) {
+      const hipError_t es = launch_tail_splitk(tail, int(splits), st);
+      if (es != hipErrorNotSupported) return es;
+    }
+    return launch_gemm_tail(tail, small, st);
   }
   switch (p.epi) {
     case Epi::Tensor:

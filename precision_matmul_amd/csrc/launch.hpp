@@ -40,6 +40,12 @@ struct GemmProblem {
   // plain problems: the launch covers output rows [row_begin, row_end)
   int64_t row_begin;
   int64_t row_end;
+  // Output addressing: row r of the result goes to out row r - out_row0.
+  // With splits > 1 (generic kernel only) the launch runs splits K ranges,
+  // range y writing its fp32 partial at out + y * split_stride elements.
+  int64_t out_row0;
+  int64_t split_stride;
+  int splits;
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st);

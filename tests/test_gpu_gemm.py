@@ -145,11 +145,13 @@ def test_blockwise_grad_weight(T, N_out, K_in):
 # gives 18 x 16 tiles and a 32-tile tail (128 x 128 tail tiles), M = 5008
 # gives 20 x 16 tiles and a 64-tile tail (256 x 128 tail tiles); elsewhere
 # the same shapes still check the full result.
-@pytest.mark.parametrize("M", [4400, 5008])
+@pytest.mark.parametrize("M,K", [(4400, 256), (5008, 256), (4400, 2048)])
 @pytest.mark.parametrize("recipe", ["tensorwise", "rowwise", "blockwise", "grad_weight", "grad_input",
                                     "tensorwise_kn"])
-def test_split_tail_rows(recipe, M):
-    N, K = 4096, 256
+def test_split_tail_rows(recipe, M, K):
+    """K = 2048 also splits the 32-tile tail of M = 4400 along K (two ranges
+    of 8 steps, fp32 partials summed by a second kernel, bias added there)."""
+    N = 4096
     if recipe == "grad_input":
         # B stored [K, N]: grad_output [M, 256] @ weight [256, 4096]
         inp = workloads.blockwise(M=M, N=K, K=N, seed=81)
