@@ -157,7 +157,8 @@ def scaled_mm_entries(A, B, scale_a, recipe_a, scale_b, recipe_b, rows, cols,
 
 def grouped_mm(A, W, offs, scale_a, scale_b, bias=None, out_dtype="bf16"):
     """MoE grouped GEMM, rowwise x rowwise.  A [M_total, K], W [E, N, K],
-    offs int32 [E] cumulative END offsets, scale_a [M_total], scale_b [E, N].
+    offs int32 [E] cumulative END offsets, scale_a [M_total], scale_b [E, N],
+    bias None, values [N] (every expert) or [E, N] (row e for expert e).
     Returns (out [M_total, N] float64 with NaN in rows no group owns,
     rows_written bool [M_total])."""
     A = np.asarray(A, np.uint8)
@@ -170,9 +171,10 @@ def grouped_mm(A, W, offs, scale_a, scale_b, bias=None, out_dtype="bf16"):
     for e in range(E):
         end = int(offs[e])
         if end > start:
+            b = None if bias is None else (np.asarray(bias)[e] if np.ndim(bias) == 2 else bias)
             out[start:end] = scaled_mm(A[start:end], W[e], scale_a[start:end],
                                        "rowwise", scale_b[e], "rowwise", "NK",
-                                       bias, out_dtype)
+                                       b, out_dtype)
             written[start:end] = True
         start = max(start, end)
     return out, written

@@ -194,6 +194,35 @@ def test_grouped_reduces_to_rowwise():
     assert np.array_equal(one, gemm.scaled_mm(qa, qw[0], sa, "rowwise", sw[0], "rowwise"))
 
 
+def test_grouped_per_expert_bias():
+    """Bias [E, N]: with all-zero activation codes every owned row of expert e
+    is exactly bf16(bias[e]) (the product vanishes, one rounding of the bias);
+    with real codes each expert equals its rowwise GEMM with bias row e."""
+    g = streams(10, 3)
+    E, N, K = 4, 32, 128
+    W = normal_bf16(g[1], (E, N, K), 0.02)
+    qw, sw = quant.quantize_rowwise(W.reshape(E * N, K))
+    qw, sw = qw.reshape(E, N, K), sw.reshape(E, N)
+    bias = quant.bf16_to_f32(normal_bf16(g[2], (E, N), 0.5))     # bf16 values
+    offs = np.array([3, 10, 10, 17], np.int32)
+    zero = np.zeros((17, K), np.uint8)
+    out, written = gemm.grouped_mm(zero, qw, offs, np.ones(17, np.float32), sw, bias=bias)
+    assert written.all()
+    rows_e = np.searchsorted(offs, np.arange(17), side="right")
+    assert np.array_equal(out, bias[rows_e].astype(np.float64))
+    act = normal_bf16(g[0], (17, K))
+    qa, sa = quant.quantize_rowwise(act)
+    out, _ = gemm.grouped_mm(qa, qw, offs, sa, sw, bias=bias)
+    start = 0
+    for e in range(E):
+        end = offs[e]
+        if end > start:
+            ref = gemm.scaled_mm(qa[start:end], qw[e], sa[start:end], "rowwise", sw[e], "rowwise",
+                                 bias=bias[e])
+            assert np.array_equal(out[start:end], ref)
+        start = end
+
+
 def test_unsupported_pairs_raise():
     z = np.zeros((2, 128), np.uint8)
     with pytest.raises(NotImplementedError):
