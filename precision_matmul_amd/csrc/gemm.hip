@@ -136,38 +136,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
     const int tn = lin / tiles_m;
     const int g = lin % tiles_m;
     if (tn >= tiles_n) return;
-    // Find expert e with prefix[e] <= g < prefix[e] + count[e].
-    int base = 0;
-    int e_found = -1, mt = 0;
-    int64_t start_found = 0, end_found = 0;
-    for (int64_t e0 = 0; e0 < p.E && e_found < 0; e0 += 64) {
-      const int64_t e = e0 + lane;
-      int64_t start = 0, end = 0;
-      if (e < p.E) {
-        end = min<int64_t>(max<int64_t>(p.offsets[e], 0), p.M);
-        start = e == 0 ? 0 : min<int64_t>(max<int64_t>(p.offsets[e - 1], 0), p.M);
-      }
-      const int cnt = end > start ? int((end - start + BM - 1) / BM) : 0;
-      int incl = cnt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += v;
-      }
-      const bool hit = (base + incl > g) && (base + incl - cnt <= g) && cnt > 0;
-      const unsigned long long mask = __ballot(hit);
-      if (mask) {
-        const int src = __builtin_ctzll(mask);
-        e_found = int(e0) + src;
-        const int excl = __shfl(incl - cnt, src, 64);
-        mt = g - base - excl;
-        start_found = __shfl(start, src, 64);
-        end_found = __shfl(end, src, 64);
-      }
-      base += __shfl(incl, 63, 64);
-    }
-    if (e_found < 0) return;
-    ti.row0 = start_found + int64_t(mt) * BM;
+    int e_found = 0;
+    int64_t end_found = 0;
+    if (!grouped_mtile(p, BM, g, e_found, ti.row0, end_found)) return;
     ti.rows_valid = int(min<int64_t>(BM, end_found - ti.row0));
     ti.n0 = int64_t(tn) * BN;
     ti.cols_valid = int(min<int64_t>(BN, p.N - ti.n0));
@@ -732,7 +703,12 @@ hipError_t launch_tail_splitk(const GemmProblem& p, int splits, hipStream_t st) 
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
-  if (p.offsets) return launch_out<Epi::Row, false, true>(p, st);
+  if (p.offsets) {
+    // grouped: the streaming kernel when its grouped loads fit the leading
+    // dimensions (K of at least 128 bytes), else 128 x 128 tiles
+    if (p.lda >= 128 && p.ldb >= 128) return launch_gemm_streaming(p, st);
+    return launch_out<Epi::Row, false, true>(p, st);
+  }
   // The streaming kernel's grouped loads need leading dimensions of at least
   // 128 bytes (256 for B stored [K, N]).  Its 256 x 256 tiles are handed out in rounds of one per CU;
   // when the last round would be less than half full, the streaming kernel

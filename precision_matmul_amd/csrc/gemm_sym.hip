@@ -72,7 +72,7 @@ __device__ __forceinline__ float fac(const v4f& f, int e) { return f[e]; }
 __device__ __forceinline__ int kswz(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
 __device__ __forceinline__ int kn_off(int k, int n) { return k * 256 + (((n >> 4) ^ kswz(k)) << 4) + (n & 15); }
 
-template <Epi EPI, bool OUT_BF16, bool BIAS, bool K_ALIGNED, bool B_KN>
+template <Epi EPI, bool OUT_BF16, bool BIAS, bool K_ALIGNED, bool B_KN, bool GROUPED>
 __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                                    int vec_out) {
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
@@ -97,10 +97,36 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  int tm, tn;
-  if (!tile_coords(tiles_m, tiles_n, tm, tn)) return;
-  const int64_t row0 = p.row_begin + int64_t(tm) * SY_BM;
-  const int rows_valid = int(min<int64_t>(SY_BM, p.M - row0));
+  // ---------------- tile ----------------
+  // Grouped (MoE) problems: tile lin = g * tiles_n + tn over the m-tiles g
+  // of all experts, so the n-tiles of one m-tile run together on one XCD and
+  // share its A rows in L2.  Expert e's B is [N, K] at B + e N K, its scales
+  // and bias rows e of [E, N].
+  int tn;
+  int64_t row0;
+  int rows_valid;
+  const uint8_t* Bg = p.B;
+  const float* sbg = p.sb;
+  [[maybe_unused]] const uint16_t* biasg = p.bias;
+  if constexpr (GROUPED) {
+    const int per_xcd = gridDim.x / 8;   // the launcher pads the grid to a multiple of 8
+    const int lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    const int g = lin / tiles_n;
+    tn = lin % tiles_n;
+    if (g >= tiles_m) return;
+    int e = 0;
+    int64_t rend = 0;
+    if (!grouped_mtile(p, SY_BM, g, e, row0, rend)) return;
+    rows_valid = int(min<int64_t>(SY_BM, rend - row0));
+    Bg = p.B + int64_t(e) * p.N * p.K;
+    sbg = p.sb + int64_t(e) * p.N;
+    if constexpr (BIAS) biasg = p.bias + int64_t(e) * p.N;
+  } else {
+    int tm;
+    if (!tile_coords(tiles_m, tiles_n, tm, tn)) return;
+    row0 = p.row_begin + int64_t(tm) * SY_BM;
+    rows_valid = int(min<int64_t>(SY_BM, p.M - row0));
+  }
   const int64_t n0 = int64_t(tn) * SY_BN;
   const int cols_valid = int(min<int64_t>(SY_BN, p.N - n0));
   const int K = int(p.K);
@@ -117,7 +143,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   const int ch_even = (lane & 7) ^ (lane >> 4);
   const int ch_odd = (lane & 7) ^ (4 | (lane >> 4));
   const Rsrc rsA = make_rsrc4(p.A + row0 * p.lda, uint32_t(rows_valid) * uint32_t(p.lda));
-  [[maybe_unused]] const Rsrc rsB = make_rsrc4(p.B + n0 * p.ldb, uint32_t(cols_valid) * uint32_t(p.ldb));
+  [[maybe_unused]] const Rsrc rsB = make_rsrc4(Bg + n0 * p.ldb, uint32_t(cols_valid) * uint32_t(p.ldb));
   const uint32_t rowA = uint32_t(wave * 32 + ld_row) * uint32_t(p.lda);
   const uint32_t rowB = uint32_t(wave * 32 + ld_row) * uint32_t(p.ldb);
   const uint32_t stepA = 8u * uint32_t(p.lda) - 1024u;   // per-q change of the per-lane offset
@@ -139,7 +165,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     if (kt >= nk) return;
     const int64_t k0 = int64_t(kt) * BK;
     const int64_t rem = (p.K - k0) * p.ldb - n0;
-    const Rsrc r = make_rsrc4(p.B + k0 * p.ldb + n0, uint32_t(rem));
+    const Rsrc r = make_rsrc4(Bg + k0 * p.ldb + n0, uint32_t(rem));
     uint32_t v[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -185,7 +211,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       sc_count = int64_t(nk) * p.M - row0 - wave * 64;
       sc_stride = p.M;
     } else if constexpr (EPI == Epi::Block128x1) {
-      sc_base = p.sb + n0 + (wave - 4) * 64;
+      sc_base = sbg + n0 + (wave - 4) * 64;
       sc_count = int64_t(nk) * p.N - n0 - (wave - 4) * 64;
       sc_stride = p.N;
     } else {
@@ -194,11 +220,11 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       const int64_t nb = n0 / 128 + (wave - 4);
       const bool in = wave < 6 && nb < p.N / 128;
       if constexpr (B_KN) {
-        sc_base = p.sb + (in ? nb : 0);
+        sc_base = sbg + (in ? nb : 0);
         sc_count = in ? int64_t(nk) * (p.N / 128) - nb : 0;
         sc_stride = p.N / 128;
       } else {
-        sc_base = p.sb + (in ? nb * nk : 0);
+        sc_base = sbg + (in ? nb * nk : 0);
         sc_count = in ? nk : 0;
         sc_stride = 1;
       }
@@ -370,16 +396,35 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     if constexpr (BLOCKWISE) load_scales(0, lds0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (row_base < rows_valid) {
 #pragma unroll
-    for (int i = 0; i < SY_FM; ++i) a[i] = read_frag(stage0, row_base + i * 16 + frow);
-    bring[0] = read_b(stage0 + SY_A, col_base);
-    if constexpr (BLOCKWISE) read_fa(stage0, fa[0], sbv[0]);
-    load_group(false, 1, lds1);
-    for (int kt = 0; kt < nk; kt += 2) {
-      step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, kt);
-      if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, kt + 1);
+      for (int i = 0; i < SY_FM; ++i) a[i] = read_frag(stage0, row_base + i * 16 + frow);
+      bring[0] = read_b(stage0 + SY_A, col_base);
+      if constexpr (BLOCKWISE) read_fa(stage0, fa[0], sbv[0]);
+      load_group(false, 1, lds1);
+      for (int kt = 0; kt < nk; kt += 2) {
+        step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, kt);
+        if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, kt + 1);
+      }
+    } else {
+      // Every row of this wave's sub-tile is past the tile's valid rows (an
+      // expert's last m-tile, or the M edge): no fragments and no MFMAs, only
+      // this wave's share of the loads, in the same order and under the same
+      // one barrier per K step as the computing waves.
+      load_group(false, 1, lds1);
+      for (int kt = 0; kt < nk; ++kt) {
+        const uint32_t this_st = (kt & 1) ? lds1 : lds0;
+        const uint32_t next_st = (kt & 1) ? lds0 : lds1;
+        load_group(true, kt + 1, next_st);
+        if constexpr (BLOCKWISE) load_scales(kt + 1, next_st);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        sy_fence();
+        asm volatile("s_barrier" ::: "memory");
+        sy_fence();
+        load_group(false, kt + 2, this_st);
+      }
     }
-    if constexpr (BLOCKWISE) {
+    if (BLOCKWISE && row_base < rows_valid) {
       // the last two results of the last step
 #pragma unroll
       for (int mm = 30; mm < 32; ++mm) {
@@ -422,8 +467,8 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       for (int e = 0; e < (SWAP ? 4 : 1); ++e) {
         const int ct = col_base + j * 16 + (SWAP ? fq * 4 + e : frow);
         const bool cin = ct < cols_valid;
-        if constexpr (EPI == Epi::Row) sbc[e] = cin ? p.sb[n0 + ct] : 0.f;
-        if constexpr (BIAS) bias_v[e] = cin ? __uint_as_float(uint32_t(p.bias[n0 + ct]) << 16) : 0.f;
+        if constexpr (EPI == Epi::Row) sbc[e] = cin ? sbg[n0 + ct] : 0.f;
+        if constexpr (BIAS) bias_v[e] = cin ? __uint_as_float(uint32_t(biasg[n0 + ct]) << 16) : 0.f;
       }
 #pragma unroll
       for (int i = 0; i < SY_FM; ++i) {
@@ -485,9 +530,12 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   }
 }
 
-template <Epi EPI, bool OUT_BF16, bool BIAS, bool B_KN>
+template <Epi EPI, bool OUT_BF16, bool BIAS, bool B_KN, bool GROUPED>
 hipError_t launch_sym(const GemmProblem& p, hipStream_t st) {
-  const int tiles_m = int((p.row_end - p.row_begin + SY_BM - 1) / SY_BM);
+  // grouped: an upper bound on the experts' m-tiles (each expert adds at most
+  // one partial tile); workgroups past the last real tile exit at once
+  const int tiles_m = GROUPED ? int((p.M + SY_BM - 1) / SY_BM + p.E)
+                              : int((p.row_end - p.row_begin + SY_BM - 1) / SY_BM);
   const int tiles_n = int((p.N + SY_BN - 1) / SY_BN);
   const int64_t tiles = int64_t(tiles_m) * tiles_n;
   if (tiles == 0) return hipSuccess;
@@ -496,28 +544,38 @@ hipError_t launch_sym(const GemmProblem& p, hipStream_t st) {
   const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
   if (BLOCKWISE || p.K % BK == 0)
-    hipLaunchKernelGGL((gemm_sym_kernel<EPI, OUT_BF16, BIAS, true, B_KN>), dim3(grid), dim3(SY_NW * 64), 0, st, p, tiles_m,
-                       tiles_n, vec_out);
+    hipLaunchKernelGGL((gemm_sym_kernel<EPI, OUT_BF16, BIAS, true, B_KN, GROUPED>), dim3(grid), dim3(SY_NW * 64), 0, st,
+                       p, tiles_m, tiles_n, vec_out);
   else if constexpr (!BLOCKWISE)
-    hipLaunchKernelGGL((gemm_sym_kernel<EPI, OUT_BF16, BIAS, false, B_KN>), dim3(grid), dim3(SY_NW * 64), 0, st, p, tiles_m,
-                       tiles_n, vec_out);
+    hipLaunchKernelGGL((gemm_sym_kernel<EPI, OUT_BF16, BIAS, false, B_KN, GROUPED>), dim3(grid), dim3(SY_NW * 64), 0,
+                       st, p, tiles_m, tiles_n, vec_out);
   return hipGetLastError();
 }
 
 template <Epi EPI>
 hipError_t launch_sym_out(const GemmProblem& p, hipStream_t st) {
   const bool bias = p.bias != nullptr;
-  if (p.b_kn) {
-    if (p.out_bf16) return bias ? launch_sym<EPI, true, true, true>(p, st) : launch_sym<EPI, true, false, true>(p, st);
-    return bias ? launch_sym<EPI, false, true, true>(p, st) : launch_sym<EPI, false, false, true>(p, st);
+  if constexpr (EPI == Epi::Row) {
+    if (p.offsets) {
+      if (p.out_bf16)
+        return bias ? launch_sym<EPI, true, true, false, true>(p, st) : launch_sym<EPI, true, false, false, true>(p, st);
+      return bias ? launch_sym<EPI, false, true, false, true>(p, st) : launch_sym<EPI, false, false, false, true>(p, st);
+    }
   }
-  if (p.out_bf16) return bias ? launch_sym<EPI, true, true, false>(p, st) : launch_sym<EPI, true, false, false>(p, st);
-  return bias ? launch_sym<EPI, false, true, false>(p, st) : launch_sym<EPI, false, false, false>(p, st);
+  if (p.b_kn) {
+    if (p.out_bf16)
+      return bias ? launch_sym<EPI, true, true, true, false>(p, st) : launch_sym<EPI, true, false, true, false>(p, st);
+    return bias ? launch_sym<EPI, false, true, true, false>(p, st) : launch_sym<EPI, false, false, true, false>(p, st);
+  }
+  if (p.out_bf16)
+    return bias ? launch_sym<EPI, true, true, false, false>(p, st) : launch_sym<EPI, true, false, false, false>(p, st);
+  return bias ? launch_sym<EPI, false, true, false, false>(p, st) : launch_sym<EPI, false, false, false, false>(p, st);
 }
 
 }  // namespace
 
-// Plain (non-grouped) GEMM, streaming schedule (B stored [N, K] or [K, N]).
+// Streaming schedule: plain GEMMs (B stored [N, K] or [K, N]) and grouped
+// rowwise GEMMs (expert weights [E, N, K]).
 hipError_t launch_gemm_streaming(const GemmProblem& p, hipStream_t st) {
   switch (p.epi) {
     case Epi::Tensor: return launch_sym_out<Epi::Tensor>(p, st);

@@ -49,7 +49,7 @@ struct GemmProblem {
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st);
-// Non-grouped GEMM with B stored [N, K] (streaming schedule, 256 x 256 tiles).
+// Streaming schedule, 256 x 256 tiles: plain GEMMs and grouped rowwise GEMMs.
 hipError_t launch_gemm_streaming(const GemmProblem& p, hipStream_t st);
 
 }  // namespace fp8mm

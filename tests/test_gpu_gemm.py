@@ -194,17 +194,19 @@ def test_split_tail_rows(recipe, M, K):
     _assert_close(out_f64(out), ref, f"split tail {recipe} {M}x{N}x{K}")
 
 
-def _grouped_case(E, N, K, sizes, seed):
-    g = workloads.streams(seed, 2)
+def _grouped_case(E, N, K, sizes, seed, with_bias=False):
+    g = workloads.streams(seed, 3)
     M = int(np.sum(sizes))
     act = workloads.normal_bf16(g[0], (M + 7, K))          # 7 trailing rows no expert owns
     W = workloads.normal_bf16(g[1], (E, N, K), 0.02)
+    bias = workloads.normal_bf16(g[2], (E, N), 0.5) if with_bias else None
     offs = np.cumsum(sizes).astype(np.int32)
     qa, sa, ra, rsa = _quant_both(act, "rowwise")
     qw, sw, rw, rsw = _quant_both(W.reshape(E * N, K), "rowwise")
     out = fp8mm.fp8_scaled_grouped_mm(qa, qw.reshape(E, N, K), torch.from_numpy(offs).cuda(), sa,
-                                      sw.reshape(E, N))
-    ref, written = gemm.grouped_mm(ra, rw.reshape(E, N, K), offs, rsa, rsw.reshape(E, N), out_dtype=None)
+                                      sw.reshape(E, N), bias=None if bias is None else bf16_dev(bias))
+    ref, written = gemm.grouped_mm(ra, rw.reshape(E, N, K), offs, rsa, rsw.reshape(E, N),
+                                   bias=None if bias is None else quant.bf16_to_f32(bias), out_dtype=None)
     got = out_f64(out)
     assert np.all(got[~written] == 0), "rows no expert owns must not be written"
     return got[written], ref[written]
@@ -214,10 +216,13 @@ def _grouped_case(E, N, K, sizes, seed):
     (8, 256, 512, [100, 0, 300, 1, 129, 0, 0, 256]),
     (3, 136, 272, [5, 260, 64]),
     (1, 128, 256, [333]),
-    (70, 64, 128, [3] * 70)])
-def test_grouped_rowwise(E, N, K, sizes):
-    got, ref = _grouped_case(E, N, K, np.array(sizes), seed=E + N + K)
-    _assert_close(got, ref, f"grouped E={E} N={N} K={K}")
+    (70, 64, 128, [3] * 70),
+    (4, 128, 64, [10, 50, 0, 70]),                       # K below 128 bytes: 128 x 128 tiles
+    (16, 384, 1024, [300, 257, 256, 255, 1, 0, 512, 40, 290, 310, 222, 260, 275, 233, 249, 301])])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_grouped_rowwise(E, N, K, sizes, with_bias):
+    got, ref = _grouped_case(E, N, K, np.array(sizes), seed=E + N + K, with_bias=with_bias)
+    _assert_close(got, ref, f"grouped E={E} N={N} K={K} bias={with_bias}")
 
 
 def test_grouped_single_expert_equals_rowwise_gemm():
