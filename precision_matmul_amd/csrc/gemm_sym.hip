@@ -239,10 +239,16 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   };
 
   // ---------------- registers ----------------
-  const int wm = wave & 3;
+  // Wave w < 4 takes rows [64 w, +64) of columns [0, 128); wave w >= 4 rows
+  // [64 ((w + 1) & 3), +64) of columns [128, 256).  The SIMD of wave w is
+  // w % 4, so the two waves of a SIMD share neither rows nor columns: a tile
+  // with only its first 64 rows valid keeps two SIMDs busy (waves 0 and 7),
+  // one with only its first 128 columns valid all four (waves 0-3).
+  const int wm = wave < 4 ? wave : (wave + 1) & 3;
   const int wn = wave >> 2;
   const int row_base = wm * SY_TM;               // sub-tile origin within the tile
   const int col_base = wn * SY_TN;
+  const bool active = row_base < rows_valid && col_base < cols_valid;   // wave-uniform
   const int frow = lane & 15;                    // fragment row (A) / column (B) of this lane
   const int fq = lane >> 4;                      // K quarter of this lane
   v4f acc[SY_FM][SY_FN];
@@ -396,7 +402,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     if constexpr (BLOCKWISE) load_scales(0, lds0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (row_base < rows_valid) {
+    if (active) {
 #pragma unroll
       for (int i = 0; i < SY_FM; ++i) a[i] = read_frag(stage0, row_base + i * 16 + frow);
       bring[0] = read_b(stage0 + SY_A, col_base);
@@ -407,10 +413,10 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
         if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, kt + 1);
       }
     } else {
-      // Every row of this wave's sub-tile is past the tile's valid rows (an
-      // expert's last m-tile, or the M edge): no fragments and no MFMAs, only
-      // this wave's share of the loads, in the same order and under the same
-      // one barrier per K step as the computing waves.
+      // Every row or every column of this wave's sub-tile is past the tile's
+      // valid ones (an expert's last m-tile, the M or N edge): no fragments
+      // and no MFMAs, only this wave's share of the loads, in the same order
+      // and under the same one barrier per K step as the computing waves.
       load_group(false, 1, lds1);
       for (int kt = 0; kt < nk; ++kt) {
         const uint32_t this_st = (kt & 1) ? lds1 : lds0;
@@ -424,7 +430,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
         load_group(false, kt + 2, this_st);
       }
     }
-    if (BLOCKWISE && row_base < rows_valid) {
+    if (BLOCKWISE && active) {
       // the last two results of the last step
 #pragma unroll
       for (int mm = 30; mm < 32; ++mm) {
