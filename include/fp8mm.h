@@ -7,16 +7,14 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer except the ones marked "host" is a DEVICE pointer owned by
- *     the caller.  Each call validates its arguments on the host, enqueues
+ *     the caller.  The library never allocates, never frees and never
+ *     synchronizes: each call validates its arguments on the host, enqueues
  *     kernels on `stream` and returns.  A NULL stream is the default stream.
- *   - Workspace: a plain (non-grouped) GEMM whose last round of output tiles
- *     would leave most compute units idle splits those rows along K.  Their
- *     fp32 partials go to a device buffer the library owns, one per (device,
- *     stream): allocated with hipMalloc on first use, grown (after
- *     synchronizing that stream) when a call needs more, kept until the
- *     process ends.  Calls on one stream reuse it in stream order; calls on
- *     different streams never share it.  If it cannot be allocated, the rows
- *     run unsplit.  No other entry point allocates, frees or synchronizes.
+ *   - Plain GEMMs may use their own output as scratch: when the last round
+ *     of output tiles would leave most compute units idle, those rows are
+ *     split along K and their fp32 partials are staged in the first rows of
+ *     `out` (only when its rows are contiguous, ldo == N), which the same
+ *     call overwrites with their results afterwards, in stream order.
  *   - Matrices are row-major with an explicit leading dimension in elements.
  *     bf16 is IEEE bfloat16 (uint16 storage); FP8 codes are uint8.
  *   - Arguments are checked synchronously before anything is enqueued; a bad

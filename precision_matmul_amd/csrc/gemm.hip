@@ -41,8 +41,6 @@
 #include "gemm_common.hpp"
 
 #include <algorithm>
-#include <mutex>
-#include <vector>
 
 namespace fp8mm {
 namespace {
@@ -611,64 +609,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, i
   }
 }
 
-// Split-K workspace: one device buffer per (device, stream), allocated on
-// first use and grown when a call needs more.  Calls on one stream use it in
-// stream order; calls on different streams use different buffers.
-hipError_t workspace_get(void** ptr, size_t bytes, hipStream_t st) {
-  struct Entry {
-    int dev;
-    hipStream_t st;
-    void* ptr;
-    size_t bytes;
-  };
-  static std::vector<Entry> cache;
-  static std::mutex mu;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(mu);
-  Entry* w = nullptr;
-  for (Entry& c : cache)
-    if (c.dev == dev && c.st == st) w = &c;
-  if (!w) {
-    cache.push_back(Entry{dev, st, nullptr, 0});
-    w = &cache.back();
-  }
-  if (w->bytes < bytes) {
-    if (w->ptr) {
-      // earlier calls on this stream may still use the old buffer
-      e = hipStreamSynchronize(st);
-      if (e != hipSuccess) return e;
-      (void)hipFree(w->ptr);
-      w->ptr = nullptr;
-      w->bytes = 0;
-    }
-    e = hipMalloc(&w->ptr, bytes);
-    if (e != hipSuccess) {
-      w->ptr = nullptr;
-      return e;
-    }
-    w->bytes = bytes;
-  }
-  *ptr = w->ptr;
-  return hipSuccess;
-}
-
-// The short tail split along K: 128 x 128 tiles x `splits` K ranges, fp32
-// partials in a workspace, then one pass that sums them, adds the bias and
-// rounds once.  Returns hipErrorNotSupported (nothing launched) when no
-// workspace can be had; the caller then runs the unsplit tail.  A tail needs
-// splits x rows x N x 4 bytes (15.7 MB for 256 rows x 5120 x 3 splits).
-hipError_t launch_tail_splitk(const GemmProblem& p, int splits, hipStream_t st) {
+// The short tail split along K: 128 x 128 tiles x `splits` K ranges write
+// fp32 partials to `scratch` (splits x rows x N floats, 16-byte aligned), then
+// one pass sums them in order, adds the bias and rounds once into the tail
+// rows of the output.
+hipError_t launch_tail_splitk(const GemmProblem& p, int splits, float* scratch, hipStream_t st) {
   const int64_t rows = p.row_end - p.row_begin;
   const int64_t slice = rows * p.N;
-  void* ws = nullptr;
-  if (workspace_get(&ws, size_t(splits) * size_t(slice) * sizeof(float), st) != hipSuccess) {
-    (void)hipGetLastError();
-    return hipErrorNotSupported;
-  }
   GemmProblem q = p;
-  q.out = ws;
+  q.out = scratch;
   q.ldo = p.N;
   q.out_bf16 = false;
   q.bias = nullptr;
@@ -676,28 +625,25 @@ hipError_t launch_tail_splitk(const GemmProblem& p, int splits, hipStream_t st) 
   q.split_stride = slice;
   q.splits = splits;
   hipError_t e = launch_gemm_tail(q, true, st);
-  if (e == hipSuccess) {
-    const int64_t threads = rows * ((p.N + 3) / 4);
-    const dim3 grid(unsigned((threads + 255) / 256));
-    const float* part = static_cast<const float*>(ws);
-    if (p.out_bf16) {
-      if (p.bias)
-        hipLaunchKernelGGL((splitk_reduce_kernel<true, true>), grid, dim3(256), 0, st, part, splits, slice, rows, p.N,
-                           p.bias, p.out, p.ldo, p.row_begin);
-      else
-        hipLaunchKernelGGL((splitk_reduce_kernel<true, false>), grid, dim3(256), 0, st, part, splits, slice, rows,
-                           p.N, p.bias, p.out, p.ldo, p.row_begin);
-    } else {
-      if (p.bias)
-        hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), grid, dim3(256), 0, st, part, splits, slice, rows,
-                           p.N, p.bias, p.out, p.ldo, p.row_begin);
-      else
-        hipLaunchKernelGGL((splitk_reduce_kernel<false, false>), grid, dim3(256), 0, st, part, splits, slice, rows,
-                           p.N, p.bias, p.out, p.ldo, p.row_begin);
-    }
-    e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = rows * ((p.N + 3) / 4);
+  const dim3 grid(unsigned((threads + 255) / 256));
+  if (p.out_bf16) {
+    if (p.bias)
+      hipLaunchKernelGGL((splitk_reduce_kernel<true, true>), grid, dim3(256), 0, st, scratch, splits, slice, rows, p.N,
+                         p.bias, p.out, p.ldo, p.row_begin);
+    else
+      hipLaunchKernelGGL((splitk_reduce_kernel<true, false>), grid, dim3(256), 0, st, scratch, splits, slice, rows,
+                         p.N, p.bias, p.out, p.ldo, p.row_begin);
+  } else {
+    if (p.bias)
+      hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), grid, dim3(256), 0, st, scratch, splits, slice, rows,
+                         p.N, p.bias, p.out, p.ldo, p.row_begin);
+    else
+      hipLaunchKernelGGL((splitk_reduce_kernel<false, false>), grid, dim3(256), 0, st, scratch, splits, slice, rows,
+                         p.N, p.bias, p.out, p.ldo, p.row_begin);
   }
-  return e;
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -723,19 +669,28 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
     GemmProblem head = p, tail = p;
     head.row_end = tm_main * 256;
     tail.row_begin = tm_main * 256;
-    const hipError_t e = launch_gemm_streaming(head, st);
-    if (e != hipSuccess) return e;
     const int64_t tail_tiles = (tiles_m - tm_main) * tiles_n;
     const bool small = 4 * tail_tiles <= cus / 2;
-    // A short tail leaves most compute units idle: split its K range so the
-    // 128 x 128 tiles times the splits cover the device, each split keeping at
-    // least 8 K steps.
+    // A short tail leaves most compute units idle: split its K range so that
+    // its 128 x 128 tiles times the splits cover the device, each split
+    // keeping at least 8 K steps.  The fp32 partials are staged in the head
+    // rows of the output (contiguous rows only), which the streaming kernel
+    // overwrites afterwards on the same stream; so the tail runs first.
     const int64_t nk = (p.K + 127) / 128;
     const int64_t splits = small ? std::min<int64_t>({cus / (4 * tail_tiles), nk / 8, 8}) : 1;
-    if (splits >= 2) {
-      const hipError_t es = launch_tail_splitk(tail, int(splits), st);
-      if (es != hipErrorNotSupported) return es;
+    if (splits >= 2 && p.ldo == p.N) {
+      const uintptr_t base = reinterpret_cast<uintptr_t>(p.out);
+      const uintptr_t scratch = (base + 255) & ~uintptr_t(255);
+      const uintptr_t head_end = base + uintptr_t(head.row_end) * uintptr_t(p.N) * (p.out_bf16 ? 2u : 4u);
+      const uintptr_t need = uintptr_t(splits) * uintptr_t(p.M - tail.row_begin) * uintptr_t(p.N) * 4u;
+      if (scratch + need <= head_end) {
+        const hipError_t e = launch_tail_splitk(tail, int(splits), reinterpret_cast<float*>(scratch), st);
+        if (e != hipSuccess) return e;
+        return launch_gemm_streaming(head, st);
+      }
     }
+    const hipError_t e = launch_gemm_streaming(head, st);
+    if (e != hipSuccess) return e;
     return launch_gemm_tail(tail, small, st);
   }
   switch (p.epi) {
