@@ -442,9 +442,8 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   }
 
   // ---------------- epilogue: scale, round, stage in LDS, 16-byte stores ----------------
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  __syncthreads();
-  uint8_t* ep = (wave < SY_NW / 2 ? stage0 : stage1) + (wave % (SY_NW / 2)) * SY_TM * EPI_PITCH;
+  // The epilogue's scale and bias loads are all issued first, so their
+  // latency overlaps the wait for the last loads and each other.
   [[maybe_unused]] float s_tensor = 0.f;
   if constexpr (EPI == Epi::Tensor) s_tensor = p.sa[0] * p.sb[0];
   // Row scales of the lane's rows: SWAP, one row per row fragment (i * 16 +
@@ -459,23 +458,52 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
         sar[i][e] = (SWAP && e > 0) ? sar[i][0] : (rt < rows_valid ? p.sa[row0 + rt] : 0.f);
       }
   }
+  // Column scales and bias of the lane's output columns: SWAP, four adjacent
+  // per column fragment j (4 fq + e); otherwise one (frow).
+  // With SWAP the four are contiguous: one 16-byte scale load and one 8-byte
+  // bias load per column fragment where alignment and the N edge allow.
+  [[maybe_unused]] float sbc[SY_FN][4];
+  [[maybe_unused]] float bias_v[SY_FN][4];
+  [[maybe_unused]] const bool sb_vec = SWAP && (reinterpret_cast<uintptr_t>(sbg) & 15) == 0;
+  [[maybe_unused]] const bool bias_vec = SWAP && (reinterpret_cast<uintptr_t>(biasg) & 7) == 0;
+#pragma unroll
+  for (int j = 0; j < SY_FN; ++j) {
+    const int c0 = col_base + j * 16 + (SWAP ? fq * 4 : frow);
+    const bool whole = SWAP && c0 + 4 <= cols_valid;
+    if constexpr (EPI == Epi::Row) {
+      if (sb_vec && whole) {
+        const v4f t = *reinterpret_cast<const v4f*>(sbg + n0 + c0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sbc[j][e] = t[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sbc[j][e] = (c0 + e < cols_valid && (SWAP || e == 0)) ? sbg[n0 + c0 + e] : 0.f;
+      }
+    }
+    if constexpr (BIAS) {
+      if (bias_vec && whole) {
+        const uint2 t = *reinterpret_cast<const uint2*>(biasg + n0 + c0);
+        bias_v[j][0] = __uint_as_float(t.x << 16);
+        bias_v[j][1] = __uint_as_float(t.x & 0xFFFF0000u);
+        bias_v[j][2] = __uint_as_float(t.y << 16);
+        bias_v[j][3] = __uint_as_float(t.y & 0xFFFF0000u);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          bias_v[j][e] = (c0 + e < cols_valid && (SWAP || e == 0))
+                             ? __uint_as_float(uint32_t(biasg[n0 + c0 + e]) << 16) : 0.f;
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+  uint8_t* ep = (wave < SY_NW / 2 ? stage0 : stage1) + (wave % (SY_NW / 2)) * SY_TM * EPI_PITCH;
 #pragma unroll
   for (int pass = 0; pass < EPI_PASSES; ++pass) {
     constexpr int FNP = SY_FN / EPI_PASSES;
 #pragma unroll
     for (int jj = 0; jj < FNP; ++jj) {
       const int j = pass * FNP + jj;
-      // output columns of the lane's values: SWAP, four adjacent (e);
-      // otherwise one
-      float sbc[4] = {0.f, 0.f, 0.f, 0.f};
-      float bias_v[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < (SWAP ? 4 : 1); ++e) {
-        const int ct = col_base + j * 16 + (SWAP ? fq * 4 + e : frow);
-        const bool cin = ct < cols_valid;
-        if constexpr (EPI == Epi::Row) sbc[e] = cin ? sbg[n0 + ct] : 0.f;
-        if constexpr (BIAS) bias_v[e] = cin ? __uint_as_float(uint32_t(biasg[n0 + ct]) << 16) : 0.f;
-      }
 #pragma unroll
       for (int i = 0; i < SY_FM; ++i) {
         float v[4];
@@ -484,8 +512,8 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
           const int ce = SWAP ? e : 0;
           v[e] = acc[i][j][e];
           if constexpr (EPI == Epi::Tensor) v[e] = v[e] * s_tensor;
-          if constexpr (EPI == Epi::Row) v[e] = (v[e] * sar[i][e]) * sbc[ce];
-          if constexpr (BIAS) v[e] = v[e] + bias_v[ce];
+          if constexpr (EPI == Epi::Row) v[e] = (v[e] * sar[i][e]) * sbc[j][ce];
+          if constexpr (BIAS) v[e] = v[e] + bias_v[j][ce];
         }
         if constexpr (SWAP) {
           uint8_t* dst = ep + (i * 16 + frow) * EPI_PITCH + (jj * 16 + fq * 4) * OUTB;
