@@ -98,10 +98,12 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---------------- tile ----------------
-  // Grouped (MoE) problems: tile lin = g * tiles_n + tn over the m-tiles g
-  // of all experts, so the n-tiles of one m-tile run together on one XCD and
-  // share its A rows in L2.  Expert e's B is [N, K] at B + e N K, its scales
-  // and bias rows e of [E, N].
+  // Grouped (MoE) problems: m-tile g of all experts (expert order) and n-tile
+  // tn go to workgroup b with b % 8 = g % 8 (workgroups are dealt to the 8
+  // XCDs round-robin), b / 8 = (g / 8) tiles_n + tn: the n-tiles of one
+  // m-tile share its A rows in one XCD's L2, and the real m-tiles (a prefix
+  // of the upper bound the grid is sized for) are spread over all XCDs.
+  // Expert e's B is [N, K] at B + e N K, its scales and bias rows e of [E, N].
   int tn;
   int64_t row0;
   int rows_valid;
@@ -109,10 +111,9 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   const float* sbg = p.sb;
   [[maybe_unused]] const uint16_t* biasg = p.bias;
   if constexpr (GROUPED) {
-    const int per_xcd = gridDim.x / 8;   // the launcher pads the grid to a multiple of 8
-    const int lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    const int g = lin / tiles_n;
-    tn = lin % tiles_n;
+    const int r = blockIdx.x / 8;
+    const int g = (r / tiles_n) * 8 + blockIdx.x % 8;
+    tn = r % tiles_n;
     if (g >= tiles_m) return;
     int e = 0;
     int64_t rend = 0;
@@ -573,7 +574,8 @@ hipError_t launch_sym(const GemmProblem& p, hipStream_t st) {
   const int tiles_n = int((p.N + SY_BN - 1) / SY_BN);
   const int64_t tiles = int64_t(tiles_m) * tiles_n;
   if (tiles == 0) return hipSuccess;
-  const int grid = int((tiles + 7) / 8 * 8);
+  // grouped: whole groups of 8 m-tiles (see the tile order in the kernel)
+  const int grid = GROUPED ? int((tiles_m + 7) / 8 * 8 * tiles_n) : int((tiles + 7) / 8 * 8);
   const int outb = OUT_BF16 ? 2 : 4;
   const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
