@@ -660,9 +660,12 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
   // when the last round would be less than half full, the streaming kernel
   // takes the rows of tiles that fill whole rounds and the rest of the rows
   // (the tail) run with 128 x 128 tiles, four times as many workgroups.
+  const int64_t tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
+  const int64_t tiles = tiles_m * tiles_n, cus = device_cus();
+  // Small problems (even 128 x 128 tiles fill at most half the device): four
+  // times as many workgroups on 128 x 128 tiles finish sooner.
+  if (4 * tiles <= cus / 2) return launch_gemm_tail(p, true, st);
   if (p.lda >= 128 && (p.b_kn ? p.ldb >= 256 : p.ldb >= 128)) {
-    const int64_t tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
-    const int64_t tiles = tiles_m * tiles_n, cus = device_cus();
     const int64_t rem = tiles % cus;
     const int64_t tm_main = tiles > cus && rem > 0 && rem <= cus / 2 ? (tiles / cus * cus) / tiles_n : tiles_m;
     if (tm_main >= tiles_m || tm_main == 0) return launch_gemm_streaming(p, st);

@@ -342,8 +342,8 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Tensorwise: clear -> amax (atomic max of the float bit pattern, valid
-// because amax >= 0) -> cast -> finalize.  The scale slot holds amax until
+// Tensorwise (beyond the single-workgroup size below): clear -> amax (atomic
+// max of the float bit pattern, valid because amax >= 0) -> cast -> finalize.  The scale slot holds amax until
 // the finalize kernel replaces it with the scale.
 // ---------------------------------------------------------------------------
 __global__ void tensor_clear_kernel(float* slot) { *reinterpret_cast<uint32_t*>(slot) = 0u; }
@@ -381,6 +381,47 @@ __global__ __launch_bounds__(256) void tensor_cast_kernel(
 
 __global__ void tensor_finalize_kernel(float* slot) { *slot = scale_from_amax(*slot, 0.0f, false); }
 
+// Small tensors (up to 1024 x 8 chunks of 8 elements): one workgroup of 1024
+// threads holds the whole tensor in registers and does amax, scale and cast
+// in a single launch.
+constexpr int kTensorSmallIt = 8;
+__global__ __launch_bounds__(1024) void tensor_small_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale) {
+  __shared__ uint32_t wmax[16];
+  const int t = threadIdx.x;
+  const int64_t chunks_per_row = cols / 8;
+  const int64_t total = rows * chunks_per_row;
+  U16x8 v[kTensorSmallIt];
+  uint32_t m = 0;
+#pragma unroll
+  for (int it = 0; it < kTensorSmallIt; ++it) {
+    const int64_t i = t + int64_t(it) * 1024;
+    if (i < total) {
+      const int64_t r = i / chunks_per_row;
+      v[it] = load16(x + r * ld_x + (i - r * chunks_per_row) * 8);
+      m = max(m, absmax8(v[it]));
+    }
+  }
+  m = wave_max(m);
+  if ((t & 63) == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  m = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) m = max(m, wmax[w]);
+  const float s = scale_from_amax(bf16_to_f32(uint16_t(m)), 0.0f, false);
+  const CastScale cs = make_cast_scale(s);
+  if (t == 0) *scale = s;
+#pragma unroll
+  for (int it = 0; it < kTensorSmallIt; ++it) {
+    const int64_t i = t + int64_t(it) * 1024;
+    if (i < total) {
+      const int64_t r = i / chunks_per_row;
+      *reinterpret_cast<uint2*>(q + r * ld_q + (i - r * chunks_per_row) * 8) = cast8(v[it], cs);
+    }
+  }
+}
+
 int grid_for(int64_t work_items, int per_block, int cap) {
   int64_t g = (work_items + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -392,6 +433,10 @@ int grid_for(int64_t work_items, int per_block, int cap) {
 hipError_t launch_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                    uint8_t* q, int64_t ld_q, float* scale, hipStream_t st) {
   const int64_t chunks = rows * (cols / 8);
+  if (chunks > 0 && chunks <= 1024 * kTensorSmallIt) {
+    hipLaunchKernelGGL(tensor_small_kernel, dim3(1), dim3(1024), 0, st, x, rows, cols, ld_x, q, ld_q, scale);
+    return hipGetLastError();
+  }
   const int g = grid_for(chunks, 256 * 8, 2048);
   hipLaunchKernelGGL(tensor_clear_kernel, dim3(1), dim3(1), 0, st, scale);
   if (chunks > 0) {

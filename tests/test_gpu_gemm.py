@@ -194,6 +194,27 @@ def test_split_tail_rows(recipe, M, K):
     _assert_close(out_f64(out), ref, f"split tail {recipe} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("pad", [0, 64])
+def test_output_rows_contiguous_or_padded(out_dtype, pad):
+    """M = 4400 has a short tail on a 256-CU device.  pad = 0: the split
+    tail's fp32 partials are staged in the output's head rows, which are then
+    overwritten.  pad = 64 (ldo > N): the rows are not contiguous, the tail
+    runs unsplit, and every padding column keeps its sentinel."""
+    M, N, K = 4400, 4096, 2048
+    inp = workloads.blockwise(M=M, N=N, K=K, seed=83)
+    qa, sa, ra, rsa = _quant_both(inp["input"], "1x128")
+    qb, sb, rb, rsb = _quant_both(inp["weight"], "128x128")
+    full = torch.full((M, N + pad), -7.0, dtype=out_dtype, device="cuda")
+    out = full[:, :N]
+    fp8mm.fp8_scaled_mm(qa, qb, sa, "1x128", sb, "128x128", out_dtype=out_dtype, out=out)
+    pad = full[:, N:]
+    assert bool((pad == -7.0).all()), "padding columns of the output were written"
+    ref = gemm.linear_forward(ra, rsa, "1x128", rb, rsb, "128x128", out_dtype=None)
+    _assert_close(out_f64(out), ref, f"padded output {out_dtype}",
+                  out_dtype="bf16" if out_dtype == torch.bfloat16 else "fp32")
+
+
 def _grouped_case(E, N, K, sizes, seed, with_bias=False):
     g = workloads.streams(seed, 3)
     M = int(np.sum(sizes))
