@@ -309,8 +309,13 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
 
   v8i a[SY_FM];
   v8i bring[2];
-  [[maybe_unused]] Fac fa[2][SY_FM];           // promotion factors of the current / next step
-  [[maybe_unused]] float sbv[2][SY_FN];
+  // Promotion factors of the current / next step.  128x1 keeps one set: the
+  // next step's value of each replaces the current one right after its last
+  // use in column 7 (the registers its per-column scales need do not allow
+  // two sets).
+  constexpr int FSETS = EPI == Epi::Block128x1 ? 1 : 2;
+  [[maybe_unused]] Fac fa[FSETS][SY_FM];
+  [[maybe_unused]] float sbv[FSETS][SY_FN];
   // Blockwise promotion runs two MFMAs behind: pending results and where they go.
   [[maybe_unused]] v4f pend_t[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
   [[maybe_unused]] Fac pend_f[2] = {Fac{}, Fac{}};
@@ -355,11 +360,11 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
           }
           pend_t[m & 1] = t;
           if constexpr (EPI == Epi::Block128x128) {
-            if (j == 0) fa[F][i] = fa[F][i] * sbv[F][0];
-            pend_f[m & 1] = fa[F][i];
+            if (j == 0) fa[F % FSETS][i] = fa[F % FSETS][i] * sbv[F % FSETS][0];
+            pend_f[m & 1] = fa[F % FSETS][i];
           } else if constexpr (!SWAP) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pend_f[m & 1][e] = fa[F][i][e] * sbv[F][j];
+            for (int e = 0; e < 4; ++e) pend_f[m & 1][e] = fa[F % FSETS][i][e] * sbv[F % FSETS][j];
           }
         }
         if constexpr (BLOCKWISE) {
@@ -380,7 +385,20 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
         if (j == SY_FN - 1) a[i] = read_frag(An, row_base + i * 16 + frow);
         // next step's promotion factors
         if constexpr (BLOCKWISE) {
-          if (j == SY_FN - 1 && i == 1) read_fa(An, fa[F ^ 1], sbv[F ^ 1]);
+          if constexpr (FSETS == 2) {
+            if (j == SY_FN - 1 && i == 1) read_fa(An, fa[F ^ 1], sbv[F ^ 1]);
+          } else if (j == SY_FN - 1) {
+            // 128x1, one set: row factors i after their last use (slot 7, i);
+            // column scales 0..6 in slot (7, 0), column 7 after slot (7, 3)
+            const float* sas_n = reinterpret_cast<const float*>(An + SY_A + SY_B);
+            const float* sbs_n = sas_n + SY_SCALE / 4;
+            if constexpr (!SWAP) fa[0][i] = *reinterpret_cast<const v4f*>(sas_n + row_base + i * 16 + fq * 4);
+            if (i == 0) {
+#pragma unroll
+              for (int jj = 0; jj < SY_FN - 1; ++jj) sbv[0][jj] = sbs_n[col_base + jj * 16 + frow];
+            }
+            if (i == SY_FM - 1) sbv[0][SY_FN - 1] = sbs_n[col_base + (SY_FN - 1) * 16 + frow];
+          }
         }
         // loads: A of step kt+2 into this stage (free after the barrier) in
         // column 7; B and the scales of step kt+1 into the other stage in
