@@ -35,20 +35,22 @@ FP8MM_HD float bf16_to_f32(uint16_t h) { return bits_f32(uint32_t(h) << 16); }
 // Scales smaller than this take the plain IEEE division path below.
 constexpr float kFastDivMinScale = 8.077935669463161e-28f;  // 2^-90
 
-// fl32(x / s) exactly (IEEE round-to-nearest) from r = fl32(1 / s):
-// q0 = x*r is within a few ulp of x/s; each FMA step forms the residual
-// x - q*s exactly and corrects q by residual*r (Markstein's correction with a
-// correctly rounded reciprocal; the second step delivers the correctly
-// rounded quotient).  Valid for s >= 2^-90 and |x/s| <= 2^100: then every
-// residual is a normal float, or x/s is below 2^-12, where every candidate
-// quotient encodes to the same (signed) zero code.
+// fl32(x / s) from r = fl32(1 / s): q0 = x*r is within one ulp of x/s; the
+// FMA forms the residual x - q0*s exactly and corrects q0 by residual*r
+// (Markstein's theorem: with a correctly rounded reciprocal one correction
+// gives the correctly rounded quotient).  Valid for s >= 2^-90 and quotients
+// of at least 2^-12 in magnitude; smaller quotients (where a subnormal
+// residual can leave the last bit off) all encode to the same signed zero
+// code.  Checked on the device over the whole input domain of the
+// quantizers: every finite bf16 x with |x| <= amax, against s = fl32(amax /
+// 448) and s = fl32(fl32(amax / 448) + 1e-12) for every positive finite bf16
+// amax with s >= 2^-90 (2 x 2.1e9 pairs): no quotient of magnitude >= 2^-12
+// differs from IEEE division and no e4m3 code differs.
 FP8MM_HD float div_by_scale(float x, float s, float r) {
 #pragma clang fp contract(off)
   const float q0 = x * r;
   const float e0 = __builtin_fmaf(-q0, s, x);
-  const float q1 = __builtin_fmaf(e0, r, q0);
-  const float e1 = __builtin_fmaf(-q1, s, x);
-  return __builtin_fmaf(e1, r, q1);
+  return __builtin_fmaf(e0, r, q0);
 }
 
 // Scale of a group from its amax: fl32(amax / 448) [+ eps], 0 -> 1.
