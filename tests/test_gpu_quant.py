@@ -165,6 +165,27 @@ def test_every_bf16_value_at_several_scales():
             _check(q, s, rq, rs, f"every bf16 {block} T={transpose}")
 
 
+def test_every_bf16_value_at_64_random_scales():
+    """The same exhaustive inputs at 64 seeded random amax values (exponent
+    and mantissa uniform over the finite bf16 range, so the scales reach from
+    the IEEE-division range below 2^-90 to ~1e35), through the rowwise
+    (with and without its epsilon) and blockwise quantizers: 33.5 M values,
+    every code against the oracle's table encoder."""
+    rng = np.random.default_rng(20260064)
+    bits = [(int(rng.integers(1, 255)) << 7) | int(rng.integers(0, 128)) for _ in range(64)]
+    x = np.concatenate([_every_bf16_under(b) for b in bits])
+    say(f"every bf16 at 64 random scales: {x.shape}")
+    xd = bf16_dev(x)
+    for eps in (0.0, None):
+        q, s = fp8mm.fp8_quantize_rowwise(xd) if eps is None else fp8mm.fp8_quantize_rowwise(xd, eps=eps)
+        rq, rs = quant.quantize_rowwise(x) if eps is None else quant.quantize_rowwise(x, eps=eps)
+        _check(q, s, rq, rs, f"rowwise every bf16, 64 scales, eps={eps}")
+    for block in ((1, 128), (128, 128), (128, 1)):
+        q, s = fp8mm.fp8_quantize_blockwise(xd, block)
+        rq, rs = quant.quantize_blockwise(x, *block)
+        _check(q, s, rq, rs, f"every bf16, 64 scales, {block}")
+
+
 def test_quantize_is_deterministic_across_runs():
     x = workloads.blockwise(M=512, N=128, K=2048)["input"]
     xd = bf16_dev(x)
