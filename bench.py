@@ -173,8 +173,20 @@ def build_workloads(torch, fp8mm, workloads):
     return W
 
 
+def copy_ceiling_gbps(torch):
+    """Measured HBM ceiling for the quantize passes: a 1 GiB device-to-device
+    copy (read + write bytes per second), median of 10."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    med, _, _, _ = time_kernel(torch, lambda: dst.copy_(src), 10)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * (1 << 30) / (med * 1e-3) / 1e9
+
+
 def time_kernel(torch, fn, iters, warmup=3):
-    """Median device time (ms) of fn's launches, HIP events on the current stream."""
+    """Device time (ms) of fn's launches, HIP events on the current stream:
+    (median, mean, min, max)."""
     for _ in range(warmup):
         fn()
     evs = []
@@ -186,7 +198,7 @@ def time_kernel(torch, fn, iters, warmup=3):
         evs.append((s, e))
     torch.cuda.synchronize()
     t = sorted(s.elapsed_time(e) for s, e in evs)
-    return t[len(t) // 2], float(np.mean(t))
+    return t[len(t) // 2], float(np.mean(t)), t[0], t[-1]
 
 
 def cpu_baseline(workloads):
@@ -332,23 +344,51 @@ def main():
     }
 
     if not args.no_recipes:
+        copy_gbs = copy_ceiling_gbps(torch)
+        result["copy_ceiling_GBps"] = round(copy_gbs, 1)
         per = {}
         for name, make in W.items():
             print(f"[bench] recipe workload {name}", file=sys.stderr, flush=True)
             w2 = wl if name == args.workload else make()
             w2["quant"]()
-            q_med, _ = time_kernel(torch, w2["quant"], 10)
-            g_med, _ = time_kernel(torch, w2["gemm"], 20)
+            q_med, _, q_min, q_max = time_kernel(torch, w2["quant"], 20)
+            g_med, _, g_min, g_max = time_kernel(torch, w2["gemm"], 50, warmup=10)
+            q_gbs = w2["quant_bytes"] / (q_med * 1e-3) / 1e9
             per[name] = {"recipe": w2["recipe"], "gemm_ms": round(g_med, 4),
+                         "gemm_ms_min_max": [round(g_min, 4), round(g_max, 4)],
                          "gemm_tflops": round(w2["flops"] / (g_med * 1e-3) / 1e12, 2),
                          "gemm_frac_fp8_peak": round(w2["flops"] / (g_med * 1e-3) / 1e12 / FP8_DENSE_PEAK_TFLOPS, 4),
                          "quant_ms": round(q_med, 4),
-                         "quant_GBps": round(w2["quant_bytes"] / (q_med * 1e-3) / 1e9, 1),
-                         "quant_frac_hbm_peak": round(w2["quant_bytes"] / (q_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                         "quant_ms_min_max": [round(q_min, 4), round(q_max, 4)],
+                         "quant_GBps": round(q_gbs, 1),
+                         "quant_frac_hbm_peak": round(q_gbs / HBM_PEAK_GBS, 4),
+                         "quant_frac_copy_ceiling": round(q_gbs / copy_gbs, 4)}
+            # HBM-bound GEMMs (the grouped MoE shape): the fraction of the
+            # attainable roofline, min(peak flops, bytes at 8 TB/s)
+            t_roof = max(w2["flops"] / (FP8_DENSE_PEAK_TFLOPS * 1e12), w2["gemm_bytes"] / (HBM_PEAK_GBS * 1e9))
+            per[name]["gemm_frac_attainable_roofline"] = round(t_roof / (g_med * 1e-3), 4)
             if w2 is not wl:
                 del w2
             torch.cuda.empty_cache()
         result["per_recipe"] = per
+        # The backward's quantize of grad_output [16640, 5120]: one dual-layout
+        # pass (1x128 codes + 128x1 codes written transposed) against the two
+        # single-layout passes it replaces.
+        print("[bench] dual-layout quantize of grad_output", file=sys.stderr, flush=True)
+        go = _dev_bf16(workloads.grad_weight()["grad_output"], torch)
+        T, C = go.shape
+        d_med, _, d_min, d_max = time_kernel(torch, lambda: fp8mm.fp8_quantize_blockwise_dual(go), 20)
+        sep_med, _, _, _ = time_kernel(torch, lambda: (fp8mm.fp8_quantize_blockwise(go, (1, 128)),
+                                                       fp8mm.fp8_quantize_blockwise(go, (128, 1), transpose_out=True)),
+                                       20)
+        dual_bytes = 4 * T * C + 4 * (T * (C // 128) + (T // 128) * C)
+        d_gbs = dual_bytes / (d_med * 1e-3) / 1e9
+        result["grad_output_dual_quant"] = {
+            "shape": [T, C], "dual_ms": round(d_med, 4), "dual_ms_min_max": [round(d_min, 4), round(d_max, 4)],
+            "two_single_passes_ms": round(sep_med, 4), "dual_GBps": round(d_gbs, 1),
+            "dual_frac_hbm_peak": round(d_gbs / HBM_PEAK_GBS, 4), "dual_frac_copy_ceiling": round(d_gbs / copy_gbs, 4),
+            "algorithmic_bytes": dual_bytes}
+        del go
 
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

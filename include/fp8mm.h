@@ -119,6 +119,29 @@ fp8mm_status fp8_quantize_blockwise(const void* x, int64_t rows, int64_t cols,
                                     uint8_t* q, int64_t ld_q, float* scale,
                                     hipStream_t stream);
 
+/* Dual-layout blockwise quantization of a linear layer's grad_output (one
+ * read of x, two results).  The backward uses grad_output twice: for
+ * grad_input = grad_output @ weight with 1x128 scales, and for grad_weight =
+ * grad_output.t() @ input with 128 tokens per scale (ColossalAI PR #6419,
+ * "Fix: Handle LowLevelZeroPlugin with use_fp8=True", Backward pass; pytorch/ao
+ * PR #2784, "improve fp8 blockwise gemm perf", the 1x128_128x128 and
+ * 1x128_128x1 tables).  The results are exactly those of
+ *   fp8_quantize_blockwise(x, ..., 1, 128, 0, q_row, ld_q_row, scale_row)
+ *   fp8_quantize_blockwise(x, ..., 128, 1, 1, q_col_t, ld_q_col, scale_col)
+ *   x:         bf16 [rows, cols], ld_x >= cols; rows and cols multiples of 128.
+ *   q_row:     uint8 [rows, cols], ld_q_row >= cols (multiple of 16);
+ *              scale_row float32 [cols/128, rows].
+ *   q_col_t:   uint8 [cols, rows] (x transposed), ld_q_col >= rows (multiple
+ *              of 16); scale_col float32 [rows/128, cols].
+ * The two outputs must not overlap each other or x.  Errors as for
+ * fp8_quantize_blockwise; shapes not divisible by 128 are FP8MM_EINVAL. */
+fp8mm_status fp8_quantize_blockwise_dual(const void* x, int64_t rows,
+                                         int64_t cols, int64_t ld_x,
+                                         uint8_t* q_row, int64_t ld_q_row,
+                                         float* scale_row, uint8_t* q_col_t,
+                                         int64_t ld_q_col, float* scale_col,
+                                         hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Scaled GEMM:  out[M, N] = sum_k (A[i,k] s_a(i,k)) (B(j,k) s_b(j,k)) (+bias[j])
  * with float32 accumulation on the matrix cores and one final rounding to

@@ -18,7 +18,7 @@ import torch
 from . import _lib
 
 __all__ = [
-    "fp8_quantize_tensorwise", "fp8_quantize_rowwise", "fp8_quantize_blockwise",
+    "fp8_quantize_tensorwise", "fp8_quantize_rowwise", "fp8_quantize_blockwise", "fp8_quantize_blockwise_dual",
     "fp8_scaled_mm", "fp8_scaled_grouped_mm", "fp8_linear_forward",
     "fp8_linear_grad_input", "fp8_linear_grad_weight", "recipe_pair_supported",
 ]
@@ -128,6 +128,26 @@ def fp8_quantize_blockwise(x, block=(1, 128), transpose_out=False):
                                             q.data_ptr(), _ld(q, "q"), s.data_ptr(), _stream(x))
     _lib.check(st, "fp8_quantize_blockwise")
     return q, s
+
+
+def fp8_quantize_blockwise_dual(x):
+    """grad_output of a linear layer, quantized once for both backward GEMMs:
+    (q_row [rows, cols], scale_row [cols/128, rows]) with 1x128 groups and
+    (q_col_t [cols, rows], scale_col [rows/128, cols]) with 128x1 groups,
+    written transposed.  rows and cols multiples of 128."""
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if rows % 128 or cols % 128:
+        raise ValueError(f"shape {tuple(x.shape)} is not a multiple of 128")
+    q_row = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s_row = torch.empty((cols // 128, rows), dtype=torch.float32, device=x.device)
+    q_col = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    s_col = torch.empty((rows // 128, cols), dtype=torch.float32, device=x.device)
+    st = _lib.load().fp8_quantize_blockwise_dual(x.data_ptr(), rows, cols, _ld(x, "x"), q_row.data_ptr(),
+                                                 _ld(q_row, "q_row"), s_row.data_ptr(), q_col.data_ptr(),
+                                                 _ld(q_col, "q_col_t"), s_col.data_ptr(), _stream(x))
+    _lib.check(st, "fp8_quantize_blockwise_dual")
+    return q_row, s_row, q_col, s_col
 
 
 def fp8_scaled_mm(A, B, scale_a, recipe_a, scale_b, recipe_b, b_layout="NK", bias=None,

@@ -24,6 +24,7 @@ SIGNATURES = {
     "fp8_quantize_tensorwise": (_i, [_p, _i64, _i64, _i64, _p, _i64, _p, _p]),
     "fp8_quantize_rowwise": (_i, [_p, _i64, _i64, _i64, _f, _p, _i64, _p, _p]),
     "fp8_quantize_blockwise": (_i, [_p, _i64, _i64, _i64, _i, _i, _i, _p, _i64, _p, _p]),
+    "fp8_quantize_blockwise_dual": (_i, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]),
     "fp8_scaled_mm": (_i, [_p, _i64, _i64, _i64, _p, _i64, _i64, _i, _p, _i, _p, _i, _p, _i, _p, _i64, _p]),
     "fp8_scaled_grouped_mm": (_i, [_p, _i64, _i64, _p, _i64, _i64, _p, _p, _p, _p, _i, _p, _i64, _p]),
     "fp8_linear_forward": (_i, [_p, _i64, _i64, _p, _i, _p, _i64, _p, _i, _p, _i, _p, _p]),

@@ -141,6 +141,27 @@ fp8mm_status fp8_quantize_blockwise(const void* x, int64_t rows, int64_t cols, i
                   "fp8_quantize_blockwise");
 }
 
+fp8mm_status fp8_quantize_blockwise_dual(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q_row,
+                                         int64_t ld_q_row, float* scale_row, uint8_t* q_col_t, int64_t ld_q_col,
+                                         float* scale_col, hipStream_t stream) {
+  fp8mm_status st = check_quant_common(x, rows, cols, ld_x, q_row, scale_row);
+  if (st != FP8MM_OK) return st;
+  if (rows > 0 && cols > 0 && (!q_col_t || !scale_row || !scale_col))
+    return fail(FP8MM_EINVAL, "null pointer argument (q_col_t, scale_row and scale_col are required)");
+  if (!aligned16(q_col_t)) return fail(FP8MM_EINVAL, "q_col_t must be 16-byte aligned");
+  if (rows % 128 != 0 || cols % 128 != 0)
+    return fail(FP8MM_EINVAL, "shape [%lld, %lld] is not a multiple of 128", (long long)rows, (long long)cols);
+  if (ld_q_row < cols || ld_q_row % 16 != 0 || ld_q_row > kMaxLd)
+    return fail(FP8MM_EINVAL, "ld_q_row (%lld) must be >= cols (%lld) and a multiple of 16", (long long)ld_q_row,
+                (long long)cols);
+  if (ld_q_col < rows || ld_q_col % 16 != 0 || ld_q_col > kMaxLd)
+    return fail(FP8MM_EINVAL, "ld_q_col (%lld) must be >= rows (%lld) and a multiple of 16", (long long)ld_q_col,
+                (long long)rows);
+  return from_hip(fp8mm::launch_quant_blockwise_dual(static_cast<const uint16_t*>(x), rows, cols, ld_x, q_row,
+                                                     ld_q_row, scale_row, q_col_t, ld_q_col, scale_col, stream),
+                  "fp8_quantize_blockwise_dual");
+}
+
 // --------------------------------------------------------------------- GEMM
 
 fp8mm_status fp8_scaled_mm(const uint8_t* A, int64_t M, int64_t K, int64_t lda, const uint8_t* B, int64_t N,

@@ -13,6 +13,11 @@ hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, i
 hipError_t launch_quant_blockwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                   int block_rows, int block_cols, int transpose_out, uint8_t* q,
                                   int64_t ld_q, float* scale, hipStream_t st);
+// One read of x, two outputs: 1x128 (row-major codes) and 128x1 written
+// transposed.  rows and cols multiples of 128.
+hipError_t launch_quant_blockwise_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                       uint8_t* q_row, int64_t ld_q_row, float* scale_row, uint8_t* q_col_t,
+                                       int64_t ld_q_col, float* scale_col, hipStream_t st);
 
 // Scale application of a GEMM.
 enum class Epi : int {

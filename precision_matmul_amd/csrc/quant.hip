@@ -261,10 +261,17 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(
 // block and stores, per column, its 8 consecutive row codes as one 8-byte
 // word.
 // ---------------------------------------------------------------------------
-template <bool TRANSPOSE>
+//
+// DUAL (with TRANSPOSE) also emits the 1x128 quantization of the same tile
+// from the same registers: row maxima over the 16 lanes that hold a row's
+// 128 columns, row scales scale_row[kb * rows + row] (kb = the tile's column
+// block), row codes q_row[row, col].  One read of x gives both operands of a
+// linear layer's backward that come from grad_output.
+template <bool TRANSPOSE, bool DUAL>
 __global__ __launch_bounds__(256) void quant_128x1_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale) {
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale,
+    uint8_t* __restrict__ q_row, int64_t ld_q_row, float* __restrict__ scale_row) {
   __shared__ U16x8 colmax[4][16];
   __shared__ float col_s[128];
   __shared__ float col_r[128];
@@ -313,6 +320,17 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(
   }
   __syncthreads();
   if (!active) return;
+  if constexpr (DUAL) {
+    // 1x128 of the tile's rows: each row's 128 columns are held by the 16
+    // consecutive lanes of one row group (cols % 128 == 0: every tile full)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t mr = group16_max(absmax8(v[i]));
+      const float sr = scale_from_amax(bf16_to_f32(uint16_t(mr)), 0.0f, false);
+      if (cc == 0) scale_row[blockIdx.x * rows + r0 + i] = sr;
+      *reinterpret_cast<uint2*>(q_row + (r0 + i) * ld_q_row + c0) = cast8(v[i], make_cast_scale(sr));
+    }
+  }
   CastScale cs[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -481,10 +499,22 @@ hipError_t launch_quant_blockwise(const uint16_t* x, int64_t rows, int64_t cols,
   } else {
     const dim3 grid(unsigned((cols + 127) / 128), unsigned(rows / 128));
     if (transpose_out)
-      hipLaunchKernelGGL(quant_128x1_kernel<true>, grid, dim3(256), 0, st, x, rows, cols, ld_x, q, ld_q, scale);
+      hipLaunchKernelGGL((quant_128x1_kernel<true, false>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q, ld_q,
+                         scale, nullptr, int64_t(0), nullptr);
     else
-      hipLaunchKernelGGL(quant_128x1_kernel<false>, grid, dim3(256), 0, st, x, rows, cols, ld_x, q, ld_q, scale);
+      hipLaunchKernelGGL((quant_128x1_kernel<false, false>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q, ld_q,
+                         scale, nullptr, int64_t(0), nullptr);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_blockwise_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                       uint8_t* q_row, int64_t ld_q_row, float* scale_row, uint8_t* q_col_t,
+                                       int64_t ld_q_col, float* scale_col, hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const dim3 grid(unsigned(cols / 128), unsigned(rows / 128));
+  hipLaunchKernelGGL((quant_128x1_kernel<true, true>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q_col_t, ld_q_col,
+                     scale_col, q_row, ld_q_row, scale_row);
   return hipGetLastError();
 }
 

@@ -186,6 +186,39 @@ def test_every_bf16_value_at_64_random_scales():
         _check(q, s, rq, rs, f"every bf16, 64 scales, {block}")
 
 
+@pytest.mark.parametrize("rows,cols", [(128, 128), (256, 384), (384, 1024)])
+def test_dual_layout_quantize_bitexact(rows, cols):
+    """One read of grad_output, both backward operands: 1x128 row codes and
+    128x1 codes written transposed, each equal to the oracle's."""
+    say(f"dual {rows}x{cols}")
+    rng = np.random.default_rng(rows * 3 + cols)
+    x = workloads.f32_to_bf16_bits((rng.standard_normal((rows, cols)) *
+                                    np.exp2(rng.integers(-20, 20, size=(rows, 1)))).astype(np.float32))
+    q_row, s_row, q_col, s_col = fp8mm.fp8_quantize_blockwise_dual(bf16_dev(x))
+    rq, rs = quant.quantize_blockwise(x, 1, 128)
+    _check(q_row, s_row, rq, rs, f"dual 1x128 {rows}x{cols}")
+    rq, rs = quant.quantize_blockwise(x, 128, 1, transpose_out=True)
+    _check(q_col, s_col, rq, rs, f"dual 128x1^T {rows}x{cols}")
+
+
+def test_dual_layout_quantize_full_size_grad_output():
+    """The grad_output of the weight-gradient workload, [16640, 5120] ~N(0,
+    1e-3): the dual pass equals the two single-layout passes everywhere, and
+    the oracle on a 256-row slab (two 128-token groups)."""
+    g = workloads.grad_weight()["grad_output"]
+    xd = bf16_dev(g)
+    q_row, s_row, q_col, s_col = fp8mm.fp8_quantize_blockwise_dual(xd)
+    a, sa = fp8mm.fp8_quantize_blockwise(xd, (1, 128))
+    b, sb = fp8mm.fp8_quantize_blockwise(xd, (128, 1), transpose_out=True)
+    assert torch.equal(q_row, a) and torch.equal(s_row, sa)
+    assert torch.equal(q_col, b) and torch.equal(s_col, sb)
+    slab = g[4096:4352]
+    rq, rs = quant.quantize_blockwise(slab, 1, 128)
+    _check(q_row[4096:4352], s_row[:, 4096:4352], rq, rs, "dual 1x128 slab")
+    rq, rs = quant.quantize_blockwise(slab, 128, 1, transpose_out=True)
+    _check(q_col[:, 4096:4352], s_col[32:34], rq, rs, "dual 128x1^T slab")
+
+
 def test_quantize_is_deterministic_across_runs():
     x = workloads.blockwise(M=512, N=128, K=2048)["input"]
     xd = bf16_dev(x)

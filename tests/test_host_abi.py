@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -118,6 +118,18 @@ def test_quantizers_reject_before_launch(lib):
     assert qb(FAKE, 128, 144, 144, 1, 128, 0, FAKE, 144, FAKE, None) == _lib.EINVAL            # cols % 128
     assert qb(FAKE, 256, 64, 64, 128, 1, 1, FAKE, 128, FAKE, None) == _lib.EINVAL              # ld_q < rows (T)
     assert qb(FAKE, 256, 64, 64, 128, 1, 2, FAKE, 256, FAKE, None) == _lib.EINVAL              # transpose flag
+
+
+def test_dual_quantizer_rejects_before_launch(lib):
+    qd = lib.fp8_quantize_blockwise_dual
+    # x, rows, cols, ld_x, q_row, ld_q_row, scale_row, q_col_t, ld_q_col, scale_col, stream
+    assert qd(FAKE, 200, 256, 256, FAKE, 256, FAKE, FAKE, 208, FAKE, None) == _lib.EINVAL       # rows % 128
+    assert qd(FAKE, 256, 144, 144, FAKE, 144, FAKE, FAKE, 256, FAKE, None) == _lib.EINVAL       # cols % 128
+    assert qd(FAKE, 256, 256, 256, FAKE, 128, FAKE, FAKE, 256, FAKE, None) == _lib.EINVAL       # ld_q_row < cols
+    assert qd(FAKE, 256, 256, 256, FAKE, 256, FAKE, FAKE, 128, FAKE, None) == _lib.EINVAL       # ld_q_col < rows
+    assert qd(FAKE, 256, 256, 256, FAKE, 256, FAKE, None, 256, FAKE, None) == _lib.EINVAL       # q_col_t NULL
+    assert qd(FAKE, 256, 256, 256, FAKE, 256, FAKE, FAKE + 8, 256, FAKE, None) == _lib.EINVAL   # alignment
+    assert qd(FAKE, 256, 256, 256, FAKE, 256, FAKE, FAKE, 256, None, None) == _lib.EINVAL       # scale_col NULL
 
 
 def test_call_forms_validate_through_scaled_mm(lib):
