@@ -389,6 +389,32 @@ def main():
             "dual_frac_hbm_peak": round(d_gbs / HBM_PEAK_GBS, 4), "dual_frac_copy_ceiling": round(d_gbs / copy_gbs, 4),
             "algorithmic_bytes": dual_bytes}
         del go
+        # The FP8 blockwise linear layer as one autograd op: forward, grad_input
+        # and grad_weight with every quantize, at the shapes of the blockwise
+        # forward, grad_input and grad_weight workloads.
+        print("[bench] linear layer step (forward + backward)", file=sys.stderr, flush=True)
+        inp = workloads.blockwise(M=16640, N=5120, K=8192)
+        xl = _dev_bf16(inp["input"], torch).requires_grad_(True)
+        wl_ = _dev_bf16(inp["weight"], torch).requires_grad_(True)
+        gl = _dev_bf16(workloads.grad_weight()["grad_output"], torch)
+        del inp
+
+        def layer_step():
+            xl.grad = None
+            wl_.grad = None
+            fp8mm.fp8_blockwise_linear(xl, wl_).backward(gl)
+
+        l_med, _, l_min, l_max = time_kernel(torch, layer_step, 10, warmup=3)
+        l_flops = 3 * 2.0 * 16640 * 5120 * 8192
+        result["linear_layer_step"] = {
+            "shape_T_Kin_Nout": [16640, 8192, 5120], "ms": round(l_med, 4),
+            "ms_min_max": [round(l_min, 4), round(l_max, 4)],
+            "tflops": round(l_flops / (l_med * 1e-3) / 1e12, 2),
+            "frac_fp8_peak": round(l_flops / (l_med * 1e-3) / 1e12 / FP8_DENSE_PEAK_TFLOPS, 4),
+            "step": "dual quantize of input, 128x128 quantize of weight, forward GEMM; dual quantize of "
+                    "grad_output, grad_input GEMM, grad_weight GEMM"}
+        del xl, wl_, gl
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

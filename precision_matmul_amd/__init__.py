@@ -21,6 +21,7 @@ __all__ = [
     "fp8_quantize_tensorwise", "fp8_quantize_rowwise", "fp8_quantize_blockwise", "fp8_quantize_blockwise_dual",
     "fp8_scaled_mm", "fp8_scaled_grouped_mm", "fp8_linear_forward",
     "fp8_linear_grad_input", "fp8_linear_grad_weight", "recipe_pair_supported",
+    "FP8BlockwiseLinear", "fp8_blockwise_linear",
 ]
 
 ROWWISE_EPS = 1e-12
@@ -288,3 +289,6 @@ def fp8_linear_grad_weight(gt_q, gt_scale, xt_q, xt_scale, out_dtype=torch.bfloa
 def recipe_pair_supported(recipe_a, recipe_b, b_layout="NK"):
     return bool(_lib.load().fp8mm_recipe_pair_supported(_recipe(recipe_a), _recipe(recipe_b),
                                                         _lib.B_LAYOUTS[b_layout]))
+
+
+from .linear import FP8BlockwiseLinear, fp8_blockwise_linear  # noqa: E402  (uses the functions above)
