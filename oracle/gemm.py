@@ -22,9 +22,12 @@ Operand conventions (all row-major numpy arrays):
               | "128x1" [K/128, N]  (128 along the contraction x 1 along N,
               named in the [K, N] orientation of the weight-gradient table of
               pytorch/ao PR #2784, "improve fp8 blockwise gemm perf")
+           A and B: "mxfp8" uint8 E8M0 bytes [M, K/32] / [N, K/32] (B as [N, K];
+              see ``mx``)
 Accepted pairs (pytorch PR #164141, "Add _scaled_mm_v2 API": one explicit
 recipe per operand, checked against a table):
   (tensorwise, tensorwise) (rowwise, rowwise) (1x128, 128x128) (1x128, 128x1)
+  (mxfp8, mxfp8)
 
 Grouped (MoE) GEMM (pytorch/ao PR #4390, "Add _grouped_mm dispatch handler to
 Float8Tensor", "Design" and review): expert e owns activation rows
@@ -44,10 +47,10 @@ invariant, transposition identities, grouped reductions, SQNR sanity floor).
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, mx
 
 PAIRS = {("tensorwise", "tensorwise"), ("rowwise", "rowwise"),
-         ("1x128", "128x128"), ("1x128", "128x1")}
+         ("1x128", "128x128"), ("1x128", "128x1"), ("mxfp8", "mxfp8")}
 
 
 def _scale_grid_A(scale, recipe, M, K):
@@ -58,6 +61,8 @@ def _scale_grid_A(scale, recipe, M, K):
         return np.repeat(s.reshape(M, 1), K, 1)
     if recipe == "1x128":
         return np.repeat(s.reshape(K // 128, M).T, 128, 1)
+    if recipe == "mxfp8":
+        return np.repeat(mx.scale_values(scale).reshape(M, K // mx.MX_BLOCK), mx.MX_BLOCK, 1)
     raise ValueError(recipe)
 
 
@@ -76,6 +81,10 @@ def _scale_grid_B_nk(scale, recipe, N, K, layout):
         return np.repeat(np.repeat(g, 128, 0), 128, 1)
     if recipe == "128x1":
         return np.repeat(s.reshape(K // 128, N).T, 128, 1)
+    if recipe == "mxfp8":
+        if layout != "NK":
+            raise NotImplementedError("mxfp8 B is read as [N, K]")
+        return np.repeat(mx.scale_values(scale).reshape(N, K // mx.MX_BLOCK), mx.MX_BLOCK, 1)
     raise ValueError(recipe)
 
 
