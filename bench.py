@@ -125,6 +125,23 @@ def build_workloads(torch, fp8mm, workloads):
                     gemm_bytes=M * K + N * K + 4 * (M + N) + 2 * N + 2 * M * N,
                     quant_bytes=3 * (M * K + N * K) + 4 * (M + N), shape=(M, N, K), recipe="rowwise_rowwise")
 
+    def mxfp8(M, N, K):
+        # the blockwise forward operands, quantized MXFP8 (E8M0 per 32 along K)
+        inp = workloads.blockwise(M=M, N=N, K=K)
+        x, w = _dev_bf16(inp["input"], torch), _dev_bf16(inp["weight"], torch)
+        state = {}
+
+        def quant():
+            state["qx"], state["sx"] = fp8mm.fp8_quantize_mx(x)
+            state["qw"], state["sw"] = fp8mm.fp8_quantize_mx(w)
+
+        def gemm():
+            return fp8mm.fp8_scaled_mm(state["qx"], state["qw"], state["sx"], "mxfp8", state["sw"], "mxfp8")
+
+        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+                    gemm_bytes=M * K + N * K + (M + N) * (K // 32) + 2 * M * N,
+                    quant_bytes=3 * (M * K + N * K) + (M + N) * (K // 32), shape=(M, N, K), recipe="mxfp8_mxfp8")
+
     def tensorwise(n):
         inp = workloads.tensorwise(n=n)
         a, b = _dev_bf16(inp["A"], torch), _dev_bf16(inp["B"], torch)
@@ -170,6 +187,7 @@ def build_workloads(torch, fp8mm, workloads):
     W["blockwise_grad_input_16640x5120x8192"] = lambda: blockwise_grad_input(16640, 8192, 5120)
     W["blockwise_grad_weight_5120x8192x16640"] = lambda: blockwise_grad_weight(16640, 5120, 8192)
     W["grouped_moe_E64_16384x1408x2048"] = grouped
+    W["mxfp8_16640x5120x8192"] = lambda: mxfp8(16640, 5120, 8192)
     return W
 
 

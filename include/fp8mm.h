@@ -57,13 +57,19 @@ typedef enum {
  *                   (the quantizer's grid of B as stored)
  *   BLOCK_128x1     B only: [K/128, N]  (128 along the contraction x 1 along
  *                   N: the weight-gradient recipe of pytorch/ao PR #2784,
- *                   "improve fp8 blockwise gemm perf", second table)     */
+ *                   "improve fp8 blockwise gemm perf", second table)
+ *   MXFP8           A: uint8 [M, K/32], B (B_NK only): uint8 [N, K/32] --
+ *                   E8M0 bytes (2^(byte - 127)), one per 32 elements along
+ *                   K, row-major; see fp8_quantize_mx.  The "mxfp8" recipe
+ *                   named by pytorch PR #164141, read as the OCP
+ *                   Microscaling format with E4M3 elements.              */
 typedef enum {
   FP8MM_TENSORWISE = 0,
   FP8MM_ROWWISE = 1,
   FP8MM_BLOCK_1x128 = 2,
   FP8MM_BLOCK_128x128 = 3,
-  FP8MM_BLOCK_128x1 = 4
+  FP8MM_BLOCK_128x1 = 4,
+  FP8MM_MXFP8 = 5
 } fp8mm_recipe;
 
 /* Storage of the B operand.  B_NK: B[N, K], K contiguous (a weight as
@@ -119,6 +125,20 @@ fp8mm_status fp8_quantize_blockwise(const void* x, int64_t rows, int64_t cols,
                                     uint8_t* q, int64_t ld_q, float* scale,
                                     hipStream_t stream);
 
+/* MXFP8 quantization (the "mxfp8" recipe of pytorch PR #164141, "Add
+ * _scaled_mm_v2 API", read as OCP Microscaling with E4M3 elements): each run
+ * of 32 consecutive elements of a row shares the power-of-two scale 2^E,
+ * E = floor(log2(amax)) - 8 clamped to [-127, 127] (an all-zero block:
+ * -127), stored as the E8M0 byte E + 127; codes are the nearest-even E4M3 of
+ * x / 2^E, saturating to +-448.
+ *   x: bf16 [rows, cols], cols % 32 == 0 (the contraction dimension of a GEMM
+ *      operand); q: uint8 [rows, cols], ld_q >= cols, multiple of 16;
+ *   scale: uint8 [rows, cols / 32], dense row-major.
+ * Errors as for fp8_quantize_blockwise. */
+fp8mm_status fp8_quantize_mx(const void* x, int64_t rows, int64_t cols,
+                             int64_t ld_x, uint8_t* q, int64_t ld_q,
+                             uint8_t* scale, hipStream_t stream);
+
 /* Dual-layout blockwise quantization of a linear layer's grad_output (one
  * read of x, two results).  The backward uses grad_output twice: for
  * grad_input = grad_output @ weight with 1x128 scales, and for grad_weight =
@@ -150,14 +170,16 @@ fp8mm_status fp8_quantize_blockwise_dual(const void* x, int64_t rows,
  * in ColossalAI PR #6419 ("Forward pass", "Backward pass").
  *   A: uint8 [M, K], leading dimension lda (K contiguous).
  *   B: uint8 [N, K] (B_NK, ldb >= K) or [K, N] (B_KN, ldb >= N).
- *   scale_a / scale_b: float32 in the layouts of fp8mm_recipe.
+ *   scale_a / scale_b: float32 in the layouts of fp8mm_recipe (MXFP8: the
+ *   pointers carry its uint8 E8M0 bytes, passed unchanged).
  *   bias: NULL or bf16 [N], added in fp32 before the rounding.
  *   out: bf16 or fp32 [M, N], leading dimension ldo >= N.
  * Accepted (recipe_a, recipe_b) pairs, anything else -> FP8MM_ENOTIMPL:
  *   (TENSORWISE, TENSORWISE)  (ROWWISE, ROWWISE)
  *   (BLOCK_1x128, BLOCK_128x128)  (BLOCK_1x128, BLOCK_128x1)
- * K % 16 == 0; blockwise recipes need K % 128 == 0 and, for BLOCK_128x128,
- * N % 128 == 0.  M, N or K of 0 is allowed. */
+ *   (MXFP8, MXFP8) with B_NK (B_KN -> FP8MM_ENOTIMPL)
+ * K % 16 == 0; blockwise and MXFP8 recipes need K % 128 == 0 and, for
+ * BLOCK_128x128, N % 128 == 0.  M, N or K of 0 is allowed. */
 fp8mm_status fp8_scaled_mm(const uint8_t* A, int64_t M, int64_t K, int64_t lda,
                            const uint8_t* B, int64_t N, int64_t ldb,
                            fp8mm_b_layout b_layout, const float* scale_a,

@@ -18,7 +18,7 @@ import torch
 from . import _lib
 
 __all__ = [
-    "fp8_quantize_tensorwise", "fp8_quantize_rowwise", "fp8_quantize_blockwise", "fp8_quantize_blockwise_dual",
+    "fp8_quantize_tensorwise", "fp8_quantize_rowwise", "fp8_quantize_blockwise", "fp8_quantize_blockwise_dual", "fp8_quantize_mx",
     "fp8_scaled_mm", "fp8_scaled_grouped_mm", "fp8_linear_forward",
     "fp8_linear_grad_input", "fp8_linear_grad_weight", "recipe_pair_supported",
     "FP8BlockwiseLinear", "fp8_blockwise_linear",
@@ -84,8 +84,12 @@ def _check_scale(scale, recipe, operand, M, N, K):
     else:
         want[3] = (N // 128) * (K // 128)
         want[4] = (K // 128) * N
+    want[5] = rows * (K // 32)
     if r in want and scale.numel() != want[r]:
         raise ValueError(f"scale_{operand} has {scale.numel()} elements, recipe needs {want[r]}")
+    want_dtype = torch.uint8 if r == 5 else torch.float32     # MXFP8: E8M0 bytes
+    if scale.dtype != want_dtype:
+        raise ValueError(f"scale_{operand} must be {want_dtype} for recipe {recipe!r}, got {scale.dtype}")
 
 
 def fp8_quantize_tensorwise(x):
@@ -131,6 +135,21 @@ def fp8_quantize_blockwise(x, block=(1, 128), transpose_out=False):
     return q, s
 
 
+def fp8_quantize_mx(x):
+    """MXFP8: (codes uint8 [rows, cols], E8M0 scale bytes uint8 [rows,
+    cols/32]); cols % 32 == 0."""
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if cols % 32:
+        raise ValueError(f"cols ({cols}) must be a multiple of 32")
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    st = _lib.load().fp8_quantize_mx(x.data_ptr(), rows, cols, _ld(x, "x"), q.data_ptr(), _ld(q, "q"),
+                                     s.data_ptr(), _stream(x))
+    _lib.check(st, "fp8_quantize_mx")
+    return q, s
+
+
 def fp8_quantize_blockwise_dual(x):
     """grad_output of a linear layer, quantized once for both backward GEMMs:
     (q_row [rows, cols], scale_row [cols/128, rows]) with 1x128 groups and
@@ -157,8 +176,6 @@ def fp8_scaled_mm(A, B, scale_a, recipe_a, scale_b, recipe_b, b_layout="NK", bia
     [N, K] (b_layout "NK") or [K, N] ("KN")."""
     _need(A, torch.uint8, "A")
     _need(B, torch.uint8, "B")
-    _need(scale_a, torch.float32, "scale_a")
-    _need(scale_b, torch.float32, "scale_b")
     if b_layout not in _lib.B_LAYOUTS:
         raise ValueError(f"b_layout must be 'NK' or 'KN', got {b_layout!r}")
     if not (scale_a.is_contiguous() and scale_b.is_contiguous()):

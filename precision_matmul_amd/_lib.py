@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfp8mm.so")
 
 OK, EINVAL, ENOTIMPL, ERUNTIME = 0, 1, 2, 3
-RECIPES = {"tensorwise": 0, "rowwise": 1, "1x128": 2, "128x128": 3, "128x1": 4}
+RECIPES = {"tensorwise": 0, "rowwise": 1, "1x128": 2, "128x128": 3, "128x1": 4, "mxfp8": 5}
 B_LAYOUTS = {"NK": 0, "KN": 1}
 OUT_BF16, OUT_FP32 = 0, 1
 
@@ -25,6 +25,7 @@ SIGNATURES = {
     "fp8_quantize_rowwise": (_i, [_p, _i64, _i64, _i64, _f, _p, _i64, _p, _p]),
     "fp8_quantize_blockwise": (_i, [_p, _i64, _i64, _i64, _i, _i, _i, _p, _i64, _p, _p]),
     "fp8_quantize_blockwise_dual": (_i, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p]),
+    "fp8_quantize_mx": (_i, [_p, _i64, _i64, _i64, _p, _i64, _p, _p]),
     "fp8_scaled_mm": (_i, [_p, _i64, _i64, _i64, _p, _i64, _i64, _i, _p, _i, _p, _i, _p, _i, _p, _i64, _p]),
     "fp8_scaled_grouped_mm": (_i, [_p, _i64, _i64, _p, _i64, _i64, _p, _p, _p, _p, _i, _p, _i64, _p]),
     "fp8_linear_forward": (_i, [_p, _i64, _i64, _p, _i, _p, _i64, _p, _i, _p, _i, _p, _p]),

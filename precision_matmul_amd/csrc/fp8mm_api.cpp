@@ -56,6 +56,7 @@ constexpr PairRule kPairs[] = {
     {FP8MM_TENSORWISE, FP8MM_TENSORWISE, fp8mm::Epi::Tensor, "tensorwise_tensorwise"},
     {FP8MM_ROWWISE, FP8MM_ROWWISE, fp8mm::Epi::Row, "rowwise_rowwise"},
     {FP8MM_BLOCK_1x128, FP8MM_BLOCK_128x128, fp8mm::Epi::Block128x128, "blockwise_1x128_128x128"},
+    {FP8MM_MXFP8, FP8MM_MXFP8, fp8mm::Epi::MX, "mxfp8_mxfp8"},
     {FP8MM_BLOCK_1x128, FP8MM_BLOCK_128x1, fp8mm::Epi::Block128x1, "blockwise_1x128_128x1"},
 };
 
@@ -65,7 +66,7 @@ const PairRule* find_pair(fp8mm_recipe a, fp8mm_recipe b) {
   return nullptr;
 }
 
-bool valid_recipe(int r) { return r >= FP8MM_TENSORWISE && r <= FP8MM_BLOCK_128x1; }
+bool valid_recipe(int r) { return r >= FP8MM_TENSORWISE && r <= FP8MM_MXFP8; }
 
 }  // namespace
 
@@ -75,7 +76,9 @@ const char* fp8mm_last_error(void) { return g_last_error; }
 
 int fp8mm_recipe_pair_supported(fp8mm_recipe recipe_a, fp8mm_recipe recipe_b, fp8mm_b_layout b_layout) {
   if (b_layout != FP8MM_B_NK && b_layout != FP8MM_B_KN) return 0;
-  return find_pair(recipe_a, recipe_b) != nullptr ? 1 : 0;
+  const PairRule* rule = find_pair(recipe_a, recipe_b);
+  if (rule && rule->epi == fp8mm::Epi::MX && b_layout != FP8MM_B_NK) return 0;
+  return rule != nullptr ? 1 : 0;
 }
 
 // ----------------------------------------------------------------- quantize
@@ -141,6 +144,19 @@ fp8mm_status fp8_quantize_blockwise(const void* x, int64_t rows, int64_t cols, i
                   "fp8_quantize_blockwise");
 }
 
+fp8mm_status fp8_quantize_mx(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                             uint8_t* scale, hipStream_t stream) {
+  fp8mm_status st = check_quant_common(x, rows, cols, ld_x, q, nullptr);
+  if (st != FP8MM_OK) return st;
+  if (!scale && rows > 0 && cols > 0) return fail(FP8MM_EINVAL, "scale must not be NULL");
+  if (cols % 32 != 0) return fail(FP8MM_EINVAL, "cols (%lld) must be a multiple of 32", (long long)cols);
+  if (ld_q < cols || ld_q % 16 != 0 || ld_q > kMaxLd)
+    return fail(FP8MM_EINVAL, "ld_q (%lld) must be >= cols (%lld) and a multiple of 16", (long long)ld_q,
+                (long long)cols);
+  return from_hip(fp8mm::launch_quant_mx(static_cast<const uint16_t*>(x), rows, cols, ld_x, q, ld_q, scale, stream),
+                  "fp8_quantize_mx");
+}
+
 fp8mm_status fp8_quantize_blockwise_dual(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q_row,
                                          int64_t ld_q_row, float* scale_row, uint8_t* q_col_t, int64_t ld_q_col,
                                          float* scale_col, hipStream_t stream) {
@@ -175,7 +191,10 @@ fp8mm_status fp8_scaled_mm(const uint8_t* A, int64_t M, int64_t K, int64_t lda, 
   if (M > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1) return fail(FP8MM_EINVAL, "M and N must be < 2^31");
   const PairRule* rule = find_pair(recipe_a, recipe_b);
   if (!rule) return fail(FP8MM_ENOTIMPL, "recipe pair (%d, %d) is not implemented", int(recipe_a), int(recipe_b));
-  const bool blockwise = rule->epi == fp8mm::Epi::Block128x128 || rule->epi == fp8mm::Epi::Block128x1;
+  const bool blockwise = rule->epi == fp8mm::Epi::Block128x128 || rule->epi == fp8mm::Epi::Block128x1 ||
+                         rule->epi == fp8mm::Epi::MX;
+  if (rule->epi == fp8mm::Epi::MX && b_layout != FP8MM_B_NK)
+    return fail(FP8MM_ENOTIMPL, "mxfp8 is implemented for B stored [N, K] only");
   if (K % 16 != 0) return fail(FP8MM_EINVAL, "K (%lld) must be a multiple of 16", (long long)K);
   if (blockwise && K % 128 != 0) return fail(FP8MM_EINVAL, "%s needs K %% 128 == 0 (K=%lld)", rule->name, (long long)K);
   if (rule->epi == fp8mm::Epi::Block128x128 && N % 128 != 0)

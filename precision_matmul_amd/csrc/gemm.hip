@@ -568,6 +568,7 @@ hipError_t launch_gemm_tail(const GemmProblem& p, bool small, hipStream_t st) {
     case Epi::Row: return launch_tail_out<Epi::Row>(p, small, st);
     case Epi::Block128x128: return launch_tail_out<Epi::Block128x128>(p, small, st);
     case Epi::Block128x1: return launch_tail_out<Epi::Block128x1>(p, small, st);
+    case Epi::MX: break;
   }
   return hipErrorInvalidValue;
 }
@@ -660,6 +661,8 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
   // when the last round would be less than half full, the streaming kernel
   // takes the rows of tiles that fill whole rounds and the rest of the rows
   // (the tail) run with 128 x 128 tiles, four times as many workgroups.
+  // MXFP8 runs on the streaming kernel only (its K % 128 == 0, B stored [N, K]).
+  if (p.epi == Epi::MX) return launch_gemm_streaming(p, st);
   const int64_t tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
   const int64_t tiles = tiles_m * tiles_n, cus = device_cus();
   // Small problems (even 128 x 128 tiles fill at most half the device): four
@@ -707,6 +710,7 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
     case Epi::Block128x1:
       return p.b_kn ? launch_out<Epi::Block128x1, true, false>(p, st)
                     : launch_out<Epi::Block128x1, false, false>(p, st);
+    case Epi::MX: break;
   }
   return hipErrorInvalidValue;
 }

@@ -21,6 +21,16 @@ __device__ __forceinline__ v4f mfma_16x16x128(const v8i& a, const v8i& b, const 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The block-scaled form.  The instruction's K order: lane group q (lanes
+// 16q .. 16q + 15) holds K [16q, 16q + 16) in bytes 0-15 and K [64 + 16q,
+// 64 + 16q + 16) in bytes 16-31 of its 32 (the fragment order of these
+// kernels, chunks q and q + 4 of a 128-byte row).  The E8M0 byte (bits 0-7)
+// that lane group g passes for its row (A) or column (B) scales K [32g,
+// 32g + 32), i.e. chunks 2g and 2g + 1.  (Probed on the device byte by byte.)
+__device__ __forceinline__ v4f mfma_16x16x128_mx(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 // LDS tile rows are 128 bytes; 16-byte chunk c of row r is stored at slot
 // c ^ ((r >> 1) & 7).  A 16x16 fragment read has 16 lanes of 16 bytes in
 // flight per LDS cycle, one per row of a 16-row group: the swizzle gives the

@@ -82,6 +82,11 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   // lane and row fragment for a 128x128 B.  A 128x1 B scales columns, so it
   // keeps the plain order (one output column and four rows per lane).
   constexpr bool SWAP = EPI != Epi::Block128x1;
+  // MXFP8: the MFMA applies the E8M0 byte of lane group g (for the lane's
+  // row or column) to K [32 g, 32 g + 32) of the step, i.e. to chunks 2g and
+  // 2g + 1, in the fragment order below.
+  constexpr bool MX = EPI == Epi::MX;
+  static_assert(!MX || (!B_KN && !GROUPED), "MXFP8: plain GEMMs with B stored [N, K]");
   using Fac = std::conditional_t<SWAP, float, v4f>;
   constexpr int OUTB = OUT_BF16 ? 2 : 4;
   constexpr int EPI_PASSES = epi_passes(SY_NW, SY_TM, SY_TN, OUTB, SY_STAGE);
@@ -233,6 +238,23 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   }
   [[maybe_unused]] auto load_scales = [&](int kt, uint32_t st) {
     if (kt >= nk) return;
+    if constexpr (MX) {
+      // E8M0 bytes of K step kt (4 per row / column): waves 0..3 rows
+      // row0 + 64 wave + lane of A, waves 4..7 columns n0 + 64 (wave - 4) +
+      // lane of B; lane l's 4 bytes land at 4 l of its wave's 256 bytes.
+      // Rows / columns past the tile edge read zeros.
+      const int64_t nkb = K / 32;                                 // bytes per row
+      const int w4 = wave & 3;
+      const int64_t first = (wave < 4 ? row0 : n0) + 64 * w4;
+      const int valid = wave < 4 ? rows_valid : cols_valid;
+      const int here = min(max(valid - 64 * w4, 0), 64);
+      const uint8_t* base = (wave < 4 ? reinterpret_cast<const uint8_t*>(p.sa) : reinterpret_cast<const uint8_t*>(sbg)) +
+                            (here > 0 ? first * nkb : 0);
+      const Rsrc r = make_rsrc4(base, uint32_t(here) * uint32_t(nkb));
+      dma_b32(r, st + SY_A + SY_B + (wave < 4 ? 0 : SY_SCALE) + w4 * 256,
+              uint32_t(lane) * uint32_t(nkb) + uint32_t(kt) * 4u);
+      return;
+    }
     const int64_t off = int64_t(kt) * sc_stride;
     const int64_t rem = sc_count - off;
     const Rsrc r = make_rsrc4(sc_base + (rem > 0 ? off : 0), uint32_t(rem > 0 ? rem * 4 : 0));
@@ -309,6 +331,13 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
 
   v8i a[SY_FM];
   v8i bring[2];
+  // MXFP8: the lane's E8M0 byte for each A fragment (its row, K range
+  // 32 fq) and for the B fragments of the ring (its column).
+  [[maybe_unused]] int mxa[SY_FM];
+  [[maybe_unused]] int mxb[2];
+  [[maybe_unused]] auto mx_byte = [&](const uint8_t* stage, int region, int idx) {
+    return int(stage[SY_A + SY_B + region + idx * 4 + fq]);
+  };
   // Promotion factors of the current / next step.  128x1 keeps one set: the
   // next step's value of each replaces the current one right after its last
   // use in column 7 (the registers its per-column scales need do not allow
@@ -344,7 +373,13 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       for (int i = 0; i < SY_FM; ++i) {
         const int m = j * SY_FM + i;     // slot in the step
         const v8i& bf = bring[j & 1];
-        if constexpr (!BLOCKWISE) {
+        if constexpr (MX) {
+          acc[i][j] = mfma_16x16x128_mx(bf, a[i], acc[i][j], mxb[j & 1], mxa[i]);
+          // Without this pin the compiler gathers the step's block-scaled
+          // MFMAs and moves the fragment reads around them, keeping all
+          // eight B fragments live (and spilling).
+          asm volatile("" : "+v"(acc[i][j]));
+        } else if constexpr (!BLOCKWISE) {
           acc[i][j] = SWAP ? mfma_16x16x128(bf, a[i], acc[i][j]) : mfma_16x16x128(a[i], bf, acc[i][j]);
         } else {
           const v4f t = SWAP ? mfma_16x16x128(bf, a[i], v4f{0.f, 0.f, 0.f, 0.f})
@@ -377,12 +412,17 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
         if (i == 0) {
           if (j + 1 < SY_FN) {
             bring[(j + 1) & 1] = read_b(Bs, col_base + (j + 1) * 16);
+            if constexpr (MX) mxb[(j + 1) & 1] = mx_byte(As, SY_SCALE, col_base + (j + 1) * 16 + frow);
           } else {
             bring[0] = read_b(An + SY_A, col_base);
+            if constexpr (MX) mxb[0] = mx_byte(An, SY_SCALE, col_base + frow);
           }
         }
         // next step's A fragment i, right after its last use
-        if (j == SY_FN - 1) a[i] = read_frag(An, row_base + i * 16 + frow);
+        if (j == SY_FN - 1) {
+          a[i] = read_frag(An, row_base + i * 16 + frow);
+          if constexpr (MX) mxa[i] = mx_byte(An, 0, row_base + i * 16 + frow);
+        }
         // next step's promotion factors
         if constexpr (BLOCKWISE) {
           if constexpr (FSETS == 2) {
@@ -405,7 +445,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
         // columns 0 and 1
         if (j == SY_FN - 1 && i == 0) load_group(false, kt + 2, this_st);
         if (j == 0 && i == 1) load_group(true, kt + 1, next_st);
-        if constexpr (BLOCKWISE) {
+        if constexpr (BLOCKWISE || MX) {
           if (j == 1 && i == 1) load_scales(kt + 1, next_st);
         }
         sy_fence();
@@ -418,7 +458,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     // step 0 in registers; the first loads of step 1 in flight.
     load_group(false, 0, lds0);
     load_group(true, 0, lds0);
-    if constexpr (BLOCKWISE) load_scales(0, lds0);
+    if constexpr (BLOCKWISE || MX) load_scales(0, lds0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (active) {
@@ -426,6 +466,11 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       for (int i = 0; i < SY_FM; ++i) a[i] = read_frag(stage0, row_base + i * 16 + frow);
       bring[0] = read_b(stage0 + SY_A, col_base);
       if constexpr (BLOCKWISE) read_fa(stage0, fa[0], sbv[0]);
+      if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < SY_FM; ++i) mxa[i] = mx_byte(stage0, 0, row_base + i * 16 + frow);
+        mxb[0] = mx_byte(stage0, SY_SCALE, col_base + frow);
+      }
       load_group(false, 1, lds1);
       for (int kt = 0; kt < nk; kt += 2) {
         step(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, kt);
@@ -441,7 +486,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
         const uint32_t this_st = (kt & 1) ? lds1 : lds0;
         const uint32_t next_st = (kt & 1) ? lds0 : lds1;
         load_group(true, kt + 1, next_st);
-        if constexpr (BLOCKWISE) load_scales(kt + 1, next_st);
+        if constexpr (BLOCKWISE || MX) load_scales(kt + 1, next_st);
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         sy_fence();
         asm volatile("s_barrier" ::: "memory");
@@ -596,7 +641,8 @@ hipError_t launch_sym(const GemmProblem& p, hipStream_t st) {
   const int grid = GROUPED ? int((tiles_m + 7) / 8 * 8 * tiles_n) : int((tiles + 7) / 8 * 8);
   const int outb = OUT_BF16 ? 2 : 4;
   const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
-  constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
+  // blockwise and MXFP8 problems have K % 128 == 0 (checked by the caller)
+  constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1 || EPI == Epi::MX;
   if (BLOCKWISE || p.K % BK == 0)
     hipLaunchKernelGGL((gemm_sym_kernel<EPI, OUT_BF16, BIAS, true, B_KN, GROUPED>), dim3(grid), dim3(SY_NW * 64), 0, st,
                        p, tiles_m, tiles_n, vec_out);
@@ -616,10 +662,12 @@ hipError_t launch_sym_out(const GemmProblem& p, hipStream_t st) {
       return bias ? launch_sym<EPI, false, true, false, true>(p, st) : launch_sym<EPI, false, false, false, true>(p, st);
     }
   }
-  if (p.b_kn) {
-    if (p.out_bf16)
-      return bias ? launch_sym<EPI, true, true, true, false>(p, st) : launch_sym<EPI, true, false, true, false>(p, st);
-    return bias ? launch_sym<EPI, false, true, true, false>(p, st) : launch_sym<EPI, false, false, true, false>(p, st);
+  if constexpr (EPI != Epi::MX) {
+    if (p.b_kn) {
+      if (p.out_bf16)
+        return bias ? launch_sym<EPI, true, true, true, false>(p, st) : launch_sym<EPI, true, false, true, false>(p, st);
+      return bias ? launch_sym<EPI, false, true, true, false>(p, st) : launch_sym<EPI, false, false, true, false>(p, st);
+    }
   }
   if (p.out_bf16)
     return bias ? launch_sym<EPI, true, true, false, false>(p, st) : launch_sym<EPI, true, false, false, false>(p, st);
@@ -636,6 +684,7 @@ hipError_t launch_gemm_streaming(const GemmProblem& p, hipStream_t st) {
     case Epi::Row: return launch_sym_out<Epi::Row>(p, st);
     case Epi::Block128x128: return launch_sym_out<Epi::Block128x128>(p, st);
     case Epi::Block128x1: return launch_sym_out<Epi::Block128x1>(p, st);
+    case Epi::MX: return p.b_kn ? hipErrorInvalidValue : launch_sym_out<Epi::MX>(p, st);
   }
   return hipErrorInvalidValue;
 }

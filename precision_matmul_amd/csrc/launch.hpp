@@ -19,12 +19,17 @@ hipError_t launch_quant_blockwise_dual(const uint16_t* x, int64_t rows, int64_t 
                                        uint8_t* q_row, int64_t ld_q_row, float* scale_row, uint8_t* q_col_t,
                                        int64_t ld_q_col, float* scale_col, hipStream_t st);
 
+// MXFP8: 32-element blocks along rows, E8M0 scale bytes [rows, cols / 32].
+hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                           uint8_t* scale, hipStream_t st);
+
 // Scale application of a GEMM.
 enum class Epi : int {
   Tensor = 0,       // out = acc * sa[0] * sb[0]
   Row = 1,          // out = acc * sa[i] * sb[j]
   Block128x128 = 2, // acc += P_kb * sa[kb, i] * sb[j/128, kb]   (per 128-K block)
-  Block128x1 = 3    // acc += P_kb * sa[kb, i] * sb[kb, j]
+  Block128x1 = 3,   // acc += P_kb * sa[kb, i] * sb[kb, j]
+  MX = 4            // MXFP8: E8M0 bytes per 32 K applied by the MFMA; out = acc
 };
 
 struct GemmProblem {

@@ -508,6 +508,49 @@ hipError_t launch_quant_blockwise(const uint16_t* x, int64_t rows, int64_t cols,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// MXFP8 (OCP Microscaling with E4M3 elements): blocks of 32 consecutive
+// elements along a row share the E8M0 byte max(exponent field of the bf16
+// amax - 8, 0), i.e. the exponent E = floor(log2 amax) - 8 clamped at -127
+// (an amax below 2^-119, a subnormal or zero block all clamp there); codes
+// are the nearest-even saturating E4M3 of x * 2^-E, an exact power-of-two
+// multiply.  Thread t handles 8 elements; four consecutive lanes are a block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_mx_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, uint8_t* __restrict__ scale) {
+  const int64_t chunks_per_row = cols / 8;      // a multiple of 4 (cols % 32 == 0)
+  const int64_t total = rows * chunks_per_row;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;   // a multiple of 4
+  // the 4 lanes of a block enter and leave the loop together: total, stride
+  // and the start of every 4-lane group are multiples of 4
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t r = i / chunks_per_row;
+    const int64_t c = (i - r * chunks_per_row) * 8;
+    const U16x8 v = load16(x + r * ld_x + c);
+    uint32_t m = absmax8(v);
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+    const int eb = int(m >> 7);                            // bf16 exponent field of amax
+    const int byte = eb > 8 ? eb - 8 : 0;                  // E + 127
+    const float mult = bits_f32(uint32_t(254 - byte) << 23);   // 2^-E
+    float xs[8], y[8];
+    unpack8(v, xs);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = xs[k] * mult;
+    *reinterpret_cast<uint2*>(q + r * ld_q + c) = make_uint2(pack4(y, xs), pack4(y + 4, xs + 4));
+    if ((threadIdx.x & 3) == 0) scale[r * (cols / 32) + c / 32] = uint8_t(byte);
+  }
+}
+
+hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                           uint8_t* scale, hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const int g = grid_for(rows * (cols / 8), 256 * 8, 4096);
+  hipLaunchKernelGGL(quant_mx_kernel, dim3(g), dim3(256), 0, st, x, rows, cols, ld_x, q, ld_q, scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_blockwise_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                        uint8_t* q_row, int64_t ld_q_row, float* scale_row, uint8_t* q_col_t,
                                        int64_t ld_q_col, float* scale_col, hipStream_t st) {

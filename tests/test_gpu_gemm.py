@@ -15,7 +15,7 @@ import torch
 
 import precision_matmul_amd as fp8mm
 import workloads
-from oracle import gemm, quant
+from oracle import gemm, mx, quant
 from tests.gpu_util import TOL_FRO, TOL_MAX, bf16_dev, host, out_f64, say
 
 pytestmark = pytest.mark.gpu
@@ -213,6 +213,45 @@ def test_output_rows_contiguous_or_padded(out_dtype, pad):
     ref = gemm.linear_forward(ra, rsa, "1x128", rb, rsb, "128x128", out_dtype=None)
     _assert_close(out_f64(out), ref, f"padded output {out_dtype}",
                   out_dtype="bf16" if out_dtype == torch.bfloat16 else "fp32")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 200, 1024), (17, 528, 256), (640, 896, 2048),
+                                   (4400, 4096, 512)])
+@pytest.mark.parametrize("with_bias,out_dtype", [(False, torch.bfloat16), (True, torch.float32)])
+def test_mxfp8_scaled_mm(M, N, K, with_bias, out_dtype):
+    """MXFP8 x MXFP8 (E8M0 per 32 along K, applied by the block-scaled MFMA)
+    against the oracle's dequantize-then-matmul on the same bf16 inputs."""
+    g = workloads.streams(M + N + K, 3)
+    x = workloads.normal_bf16(g[0], (M, K))
+    w = workloads.normal_bf16(g[1], (N, K), 0.02)
+    bias = workloads.normal_bf16(g[2], (N,), 0.01) if with_bias else None
+    qa, sa = fp8mm.fp8_quantize_mx(bf16_dev(x))
+    qb, sb = fp8mm.fp8_quantize_mx(bf16_dev(w))
+    ra, rsa = mx.quantize_mx(x)
+    rb, rsb = mx.quantize_mx(w)
+    assert np.array_equal(host(qa), ra) and np.array_equal(host(sa), rsa)
+    out = fp8mm.fp8_scaled_mm(qa, qb, sa, "mxfp8", sb, "mxfp8", out_dtype=out_dtype,
+                              bias=None if bias is None else bf16_dev(bias))
+    ref = gemm.scaled_mm(ra, rb, rsa, "mxfp8", rsb, "mxfp8",
+                         bias=None if bias is None else quant.bf16_to_f32(bias), out_dtype=None)
+    _assert_close(out_f64(out), ref, f"mxfp8 {M}x{N}x{K} bias={with_bias}",
+                  out_dtype="bf16" if out_dtype == torch.bfloat16 else "fp32")
+
+
+def test_full_mxfp8_sampled():
+    """The blockwise forward shape 16640x5120x8192 in MXFP8, sampled entries."""
+    M, N, K = 16640, 5120, 8192
+    inp = workloads.blockwise(M=M, N=N, K=K)
+    x, w = inp["input"], inp["weight"]
+    qa, sa = fp8mm.fp8_quantize_mx(bf16_dev(x))
+    qb, sb = fp8mm.fp8_quantize_mx(bf16_dev(w))
+    out = out_f64(fp8mm.fp8_scaled_mm(qa, qb, sa, "mxfp8", sb, "mxfp8"))
+    I = _sample(M, 64, 11)
+    J = _sample(N, 64, 12)
+    ra, rsa = mx.quantize_mx(x[I])
+    rb, rsb = mx.quantize_mx(w[J])
+    ref = gemm.scaled_mm(ra, rb, rsa, "mxfp8", rsb, "mxfp8", out_dtype=None)
+    _assert_close(out[np.ix_(I, J)], ref, "mxfp8 16640x5120x8192 sampled")
 
 
 def _grouped_case(E, N, K, sizes, seed, with_bias=False):

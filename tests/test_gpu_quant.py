@@ -7,7 +7,7 @@ import torch
 
 import precision_matmul_amd as fp8mm
 import workloads
-from oracle import e4m3, quant
+from oracle import e4m3, mx, quant
 from tests.gpu_util import bf16_dev, host, say
 
 pytestmark = pytest.mark.gpu
@@ -217,6 +217,46 @@ def test_dual_layout_quantize_full_size_grad_output():
     _check(q_row[4096:4352], s_row[:, 4096:4352], rq, rs, "dual 1x128 slab")
     rq, rs = quant.quantize_blockwise(slab, 128, 1, transpose_out=True)
     _check(q_col[:, 4096:4352], s_col[32:34], rq, rs, "dual 128x1^T slab")
+
+
+def _check_mx(q_gpu, s_gpu, q_ref, s_ref, what):
+    qg, sg = host(q_gpu), host(s_gpu)
+    assert qg.shape == q_ref.shape and sg.shape == s_ref.shape, (what, qg.shape, sg.shape)
+    bad_s = np.argwhere(sg != s_ref)
+    assert bad_s.size == 0, (what, "scale bytes differ at", bad_s[:8], sg[tuple(bad_s[0])], s_ref[tuple(bad_s[0])])
+    bad = np.argwhere(qg != q_ref)
+    assert bad.size == 0, (what, "codes differ at", bad[:8], qg[tuple(bad[0])], q_ref[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 96), (256, 1024), (64, 8192)])
+def test_mx_quantize_bitexact(rows, cols):
+    say(f"mx {rows}x{cols}")
+    rng = np.random.default_rng(rows * 5 + cols)
+    x = workloads.f32_to_bf16_bits((rng.standard_normal((rows, cols)) *
+                                    np.exp2(rng.integers(-60, 60, size=(rows, 1)))).astype(np.float32))
+    q, s = fp8mm.fp8_quantize_mx(bf16_dev(x))
+    rq, rs = mx.quantize_mx(x)
+    _check_mx(q, s, rq, rs, f"mx {rows}x{cols}")
+
+
+def test_mx_quantize_every_bf16_and_special_blocks():
+    """Every bf16 value at six block maxima (the 32-blocks of these matrices
+    have maxima of every size below the chosen one), zero blocks, blocks of
+    subnormals and blocks whose maximum saturates."""
+    amaxes = [448.0, 1.0, 3.140625, 61440.0, 2.0 ** -20, 1e-30]
+    bits = workloads.f32_to_bf16_bits(np.array(amaxes, np.float32))
+    x = np.concatenate([_every_bf16_under(int(b)) for b in bits])
+    special = np.zeros((4, 128), np.float32)
+    special[1, :32] = 2.0 ** -130
+    special[1, 32:64] = -(2.0 ** -133)
+    special[2, :32] = 1.0
+    special[2, 7] = 1.99                      # quotient ~509: saturates
+    special[3] = np.linspace(-3e38, 3e38, 128, dtype=np.float32)
+    sb = workloads.f32_to_bf16_bits(special)
+    x = np.concatenate([x, np.tile(sb, (1, x.shape[1] // 128))])
+    q, s = fp8mm.fp8_quantize_mx(bf16_dev(x))
+    rq, rs = mx.quantize_mx(x)
+    _check_mx(q, s, rq, rs, "mx every bf16 + special blocks")
 
 
 def test_quantize_is_deterministic_across_runs():

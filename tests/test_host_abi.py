@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -44,7 +44,8 @@ def test_recipe_pair_table(lib):
     for a in R:
         for b in R:
             for layout in (0, 1):
-                assert lib.fp8mm_recipe_pair_supported(R[a], R[b], layout) == int((a, b) in ok), (a, b)
+                want = (a, b) in ok or ((a, b) == ("mxfp8", "mxfp8") and layout == 0)
+                assert lib.fp8mm_recipe_pair_supported(R[a], R[b], layout) == int(want), (a, b, layout)
     assert lib.fp8mm_recipe_pair_supported(0, 0, 7) == 0
 
 
@@ -75,6 +76,10 @@ def _mm(lib, **kw):
     (dict(ra=2, rb=3, K=144, lda=144, ldb=144), _lib.EINVAL),      # blockwise K % 128
     (dict(ra=2, rb=3, N=100, ldo=100), _lib.EINVAL),               # 128x128 needs N % 128
     (dict(ra=0, rb=0, layout=1, ldb=32), _lib.EINVAL),             # KN: ldb >= N
+    (dict(ra=5, rb=5, layout=1), _lib.ENOTIMPL),                   # mxfp8 with B stored [K, N]
+    (dict(ra=5, rb=5, K=160, lda=160, ldb=160), _lib.EINVAL),      # mxfp8 K % 128
+    (dict(ra=5, rb=2), _lib.ENOTIMPL),                             # mxfp8 x 1x128
+    (dict(ra=6), _lib.EINVAL),                                     # unknown enum
 ])
 def test_scaled_mm_rejects_before_launch(lib, kw, code):
     assert _mm(lib, **kw) == code
@@ -130,6 +135,15 @@ def test_dual_quantizer_rejects_before_launch(lib):
     assert qd(FAKE, 256, 256, 256, FAKE, 256, FAKE, None, 256, FAKE, None) == _lib.EINVAL       # q_col_t NULL
     assert qd(FAKE, 256, 256, 256, FAKE, 256, FAKE, FAKE + 8, 256, FAKE, None) == _lib.EINVAL   # alignment
     assert qd(FAKE, 256, 256, 256, FAKE, 256, FAKE, FAKE, 256, None, None) == _lib.EINVAL       # scale_col NULL
+
+
+def test_mx_quantizer_rejects_before_launch(lib):
+    qm = lib.fp8_quantize_mx
+    # x, rows, cols, ld_x, q, ld_q, scale, stream
+    assert qm(FAKE, 4, 48, 48, FAKE, 48, FAKE, None) == _lib.EINVAL        # cols % 32
+    assert qm(FAKE, 4, 64, 64, FAKE, 48, FAKE, None) == _lib.EINVAL        # ld_q < cols
+    assert qm(FAKE, 4, 64, 64, FAKE, 64, None, None) == _lib.EINVAL        # scale NULL
+    assert qm(FAKE, 4, 64, 64, FAKE + 4, 64, FAKE, None) == _lib.EINVAL    # alignment
 
 
 def test_call_forms_validate_through_scaled_mm(lib):
