@@ -72,6 +72,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
   constexpr int FN = TN / 16;
   constexpr int D = STAGES - 1;          // prefetch distance in K steps
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
+  // MXFP8: E8M0 bytes per 32 K, 4 per row / column per K step, loaded like
+  // the blockwise scales and applied by the block-scaled MFMA.
+  constexpr bool MX = EPI == Epi::MX;
+  static_assert(!MX || (!B_KN && !GROUPED), "MXFP8: plain GEMMs with B stored [N, K]");
   constexpr int A_BYTES = BM * BK;
   constexpr int B_BYTES = BN * BK;
   // Scale regions (blockwise): 8 chunks of 256 bytes, 4 for sA (BM = 256
@@ -79,8 +83,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
   // scale per 128 columns, at the start of its chunk).  Each chunk is filled
   // by one wave's 64 lanes: a lane whose DMA offset is out of range still
   // writes (zeros) to its LDS slot, so a wave must own its whole chunk.
-  constexpr int SA_BYTES = BLOCKWISE ? 1024 : 0;
-  constexpr int SB_BYTES = BLOCKWISE ? 1024 : 0;
+  constexpr int SA_BYTES = BLOCKWISE || MX ? 1024 : 0;
+  constexpr int SB_BYTES = BLOCKWISE || MX ? 1024 : 0;
   constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
   constexpr int OUTB = OUT_BF16 ? 2 : 4;
   constexpr int EPI_PASSES = epi_passes(NW, TM, TN, OUTB, STAGE);
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
   constexpr int NCH = BN / 16;                       // KN loader: 16-byte chunks per k row
   constexpr int KR = B_KN ? BK * NCH / NT : 1;       // KN loader: k rows per thread
   constexpr int LKN = B_KN ? KR : 0;
-  constexpr int LS = BLOCKWISE ? 8 / NW : 0;
+  constexpr int LS = BLOCKWISE || MX ? 8 / NW : 0;
   constexpr int LPS = LA + LB + LKN + LS;
   static_assert((NW == 4 || NW == 8) && NW % 2 == 0, "4 or 8 waves");
   static_assert(STAGES == 2 || STAGES == 3, "2 or 3 stages");
@@ -197,6 +201,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
       uint32_t vo = voffB[qb];
       if (tail) vo = (int(k0) + ld_chunk * 16 < K) ? vo : 0x80000000u;
       dma_b128(r, st + A_BYTES + (qb * NW + wave) * 1024, vo, k0);
+    } else if constexpr (MX) {
+      // chunk c < 4: E8M0 bytes of A rows row0 + 64c + lane; c >= 4: of B
+      // columns n0 + 64(c - 4) + lane; 4 bytes (K step kt) per lane at 4 lane
+      const int c = (q - LA - LB) * NW + wave;
+      const int64_t nkb = K / 32;
+      const int w4 = c & 3;
+      const int64_t first = (c < 4 ? ti.row0 : ti.n0) + 64 * w4;
+      const int valid = c < 4 ? ti.rows_valid : ti.cols_valid;
+      const int here = live ? min(max(valid - 64 * w4, 0), 64) : 0;
+      const uint8_t* base = (c < 4 ? reinterpret_cast<const uint8_t*>(p.sa) : reinterpret_cast<const uint8_t*>(ti.sb)) +
+                            (here > 0 ? first * nkb : 0);
+      const Rsrc r = make_rsrc4(base, uint32_t(here) * uint32_t(nkb));
+      dma_b32(r, st + A_BYTES + B_BYTES + (c < 4 ? 0 : SA_BYTES) + w4 * 256,
+              uint32_t(lane) * uint32_t(nkb) + uint32_t(kt) * 4u);
     } else if constexpr (BLOCKWISE) {
       const int c = (q - LA - LB) * NW + wave;        // scale chunk 0..7 of this wave
       if (c < 4) {
@@ -308,6 +326,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
     v8i b[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) b[j] = read_frag(Bs, col_base + j * 16 + frow);
+    // MXFP8: the lane's E8M0 byte for its row / column and lane group fq
+    [[maybe_unused]] const uint8_t* sab = As + A_BYTES + B_BYTES;
+    [[maybe_unused]] int mxb[FN];
+    [[maybe_unused]] int mxa_cur = 0;
+    if constexpr (MX) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mxb[j] = sab[SA_BYTES + (col_base + j * 16 + frow) * 4 + fq];
+      mxa_cur = sab[(row_base + frow) * 4 + fq];
+    }
     [[maybe_unused]] float sbk = 0.f;
     [[maybe_unused]] float sbv[FN];
     [[maybe_unused]] v4f fa_cur;
@@ -327,11 +354,21 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
       for (int q = i * LDIRECT / FM; q < (i + 1) * LDIRECT / FM; ++q) issue_one(q, (S + D) % STAGES, kt + D, live_next);
       v8i a_next = a_cur;
       [[maybe_unused]] v4f fa_next;
+      [[maybe_unused]] int mxa_next = mxa_cur;
       if (i + 1 < FM) {
         a_next = read_frag(As, row_base + (i + 1) * 16 + frow);
+        if constexpr (MX) mxa_next = sab[(row_base + (i + 1) * 16 + frow) * 4 + fq];
         if constexpr (BLOCKWISE) fa_next = *reinterpret_cast<const v4f*>(sas + row_base + (i + 1) * 16 + fq * 4);
       }
-      if constexpr (!BLOCKWISE) {
+      if constexpr (MX) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          acc[i][j] = mfma_16x16x128_mx(a_cur, b[j], acc[i][j], mxa_cur, mxb[j]);
+          asm volatile("" : "+v"(acc[i][j]));   // keeps the compiler's order (see the streaming kernel)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mxa_cur = mxa_next;
+      } else if constexpr (!BLOCKWISE) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           acc[i][j] = mfma_16x16x128(a_cur, b[j], acc[i][j]);
@@ -491,7 +528,8 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t st) {
   const int grid = int((tiles + 7) / 8 * 8);
   const int outb = p.out_bf16 ? 2 : 4;
   const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
-  constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
+  // blockwise and MXFP8 problems have K % 128 == 0 (checked by the caller)
+  constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1 || EPI == Epi::MX;
   if (BLOCKWISE || p.K % BK == 0)
     hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, EPI, B_KN, OUT_BF16, BIAS, GROUPED, true>),
                        dim3(grid, max(1, p.splits)), dim3(WM * WN * 64), 0, st, p, tiles_m, tiles_n, vec_out);
@@ -546,9 +584,11 @@ static int device_cus() {
 // [K, N]: 4 waves), which run closer to the streaming kernel's rate.
 template <Epi EPI, bool OUT_BF16, bool BIAS>
 hipError_t launch_tail(const GemmProblem& p, bool small, hipStream_t st) {
-  if (p.b_kn) {
-    if (small) return launch_cfg<128, 128, 2, 2, 3, EPI, true, OUT_BF16, BIAS, false>(p, st);
-    return launch_cfg<256, 128, 2, 2, 3, EPI, true, OUT_BF16, BIAS, false>(p, st);
+  if constexpr (EPI != Epi::MX) {
+    if (p.b_kn) {
+      if (small) return launch_cfg<128, 128, 2, 2, 3, EPI, true, OUT_BF16, BIAS, false>(p, st);
+      return launch_cfg<256, 128, 2, 2, 3, EPI, true, OUT_BF16, BIAS, false>(p, st);
+    }
   }
   if (small) return launch_cfg<128, 128, 2, 2, 3, EPI, false, OUT_BF16, BIAS, false>(p, st);
   return launch_cfg<256, 128, 4, 2, 3, EPI, false, OUT_BF16, BIAS, false>(p, st);
@@ -568,7 +608,7 @@ hipError_t launch_gemm_tail(const GemmProblem& p, bool small, hipStream_t st) {
     case Epi::Row: return launch_tail_out<Epi::Row>(p, small, st);
     case Epi::Block128x128: return launch_tail_out<Epi::Block128x128>(p, small, st);
     case Epi::Block128x1: return launch_tail_out<Epi::Block128x1>(p, small, st);
-    case Epi::MX: break;
+    case Epi::MX: return p.b_kn ? hipErrorInvalidValue : launch_tail_out<Epi::MX>(p, small, st);
   }
   return hipErrorInvalidValue;
 }
@@ -661,8 +701,6 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
   // when the last round would be less than half full, the streaming kernel
   // takes the rows of tiles that fill whole rounds and the rest of the rows
   // (the tail) run with 128 x 128 tiles, four times as many workgroups.
-  // MXFP8 runs on the streaming kernel only (its K % 128 == 0, B stored [N, K]).
-  if (p.epi == Epi::MX) return launch_gemm_streaming(p, st);
   const int64_t tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
   const int64_t tiles = tiles_m * tiles_n, cus = device_cus();
   // Small problems (even 128 x 128 tiles fill at most half the device): four
@@ -710,7 +748,7 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
     case Epi::Block128x1:
       return p.b_kn ? launch_out<Epi::Block128x1, true, false>(p, st)
                     : launch_out<Epi::Block128x1, false, false>(p, st);
-    case Epi::MX: break;
+    case Epi::MX: return p.b_kn ? hipErrorInvalidValue : launch_out<Epi::MX, false, false>(p, st);
   }
   return hipErrorInvalidValue;
 }

@@ -216,11 +216,14 @@ def test_output_rows_contiguous_or_padded(out_dtype, pad):
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 200, 1024), (17, 528, 256), (640, 896, 2048),
-                                   (4400, 4096, 512)])
+                                   (4400, 4096, 512), (4400, 4096, 2048)])
 @pytest.mark.parametrize("with_bias,out_dtype", [(False, torch.bfloat16), (True, torch.float32)])
 def test_mxfp8_scaled_mm(M, N, K, with_bias, out_dtype):
     """MXFP8 x MXFP8 (E8M0 per 32 along K, applied by the block-scaled MFMA)
-    against the oracle's dequantize-then-matmul on the same bf16 inputs."""
+    against the oracle's dequantize-then-matmul on the same bf16 inputs.
+    The shapes reach every launch path: small problems on 128 x 128 tiles
+    only, the streaming kernel with a 128 x 128 tail (4400 x 4096 x 512) and
+    with a tail split along K (4400 x 4096 x 2048)."""
     g = workloads.streams(M + N + K, 3)
     x = workloads.normal_bf16(g[0], (M, K))
     w = workloads.normal_bf16(g[1], (N, K), 0.02)
