@@ -15,7 +15,8 @@ computes, written from the definitions:
   epsilon) and blockwise (1x128, 128x128, 128x1) groupings.
 * ``gemm``  - the scaled matrix multiply evaluated as "dequantize both operands,
   then one matmul" in float64, rounded once to the output dtype; the grouped
-  (MoE) variant and the three linear call forms are reductions to it.
+  (MoE) variants (forward, input gradient, per-expert weight gradient) and the
+  three linear call forms are reductions to it.
 
 It shares no code, tables or constants with the HIP library, and imports
 nothing from it.  Every floating-point step is numpy float32 (where the method

@@ -32,7 +32,11 @@ recipe per operand, checked against a table):
 Grouped (MoE) GEMM (pytorch/ao PR #4390, "Add _grouped_mm dispatch handler to
 Float8Tensor", "Design" and review): expert e owns activation rows
 [offs[e-1], offs[e]) (offs[-1] = 0), weights are [E, N, K] and are used in the
-form grouped_mm(act, weight.transpose(-2, -1)); rowwise scales only.
+form grouped_mm(act, weight.transpose(-2, -1)); the pages give rowwise scales.
+Readings beyond the pages: the blockwise recipe applied per expert in the same
+grouped form (1x128 activations, 128x128 expert weights), the input gradient
+as the grouped GEMM reading each expert's weight as [K, N], and the weight
+gradient per expert over the expert's own tokens (``grouped_grad_weight``).
 
 Linear call forms (ColossalAI PR #6419 "Forward pass" / "Backward pass";
 pytorch/ao PR #2784 tables):
@@ -47,7 +51,7 @@ invariant, transposition identities, grouped reductions, SQNR sanity floor).
 
 import numpy as np
 
-from . import e4m3, mx
+from . import e4m3, mx, quant
 
 PAIRS = {("tensorwise", "tensorwise"), ("rowwise", "rowwise"),
          ("1x128", "128x128"), ("1x128", "128x1"), ("mxfp8", "mxfp8")}
@@ -164,16 +168,30 @@ def scaled_mm_entries(A, B, scale_a, recipe_a, scale_b, recipe_b, rows, cols,
     return round_out(vals, out_dtype)
 
 
-def grouped_mm(A, W, offs, scale_a, scale_b, bias=None, out_dtype="bf16"):
-    """MoE grouped GEMM, rowwise x rowwise.  A [M_total, K], W [E, N, K],
-    offs int32 [E] cumulative END offsets, scale_a [M_total], scale_b [E, N],
-    bias None, values [N] (every expert) or [E, N] (row e for expert e).
+GROUPED_PAIRS = {("rowwise", "rowwise"), ("1x128", "128x128")}
+
+
+def grouped_mm(A, W, offs, scale_a, scale_b, bias=None, out_dtype="bf16",
+               recipe_a="rowwise", recipe_b="rowwise", layout="NK"):
+    """MoE grouped GEMM: rows [offs[e-1], offs[e]) of A times expert e's B.
+    A [M_total, K]; W [E, N, K] (layout "NK", the forward's
+    grouped_mm(act, weight.transpose(-2, -1))) or [E, K, N] (layout "KN", e.g.
+    the stored [E, N_out, K_in] weights read by the input gradient, which
+    contracts over N_out); offs int32 [E] cumulative END offsets.
+    Recipes: rowwise x rowwise (scale_a [M_total], scale_b [E, N]) or
+    1x128 x 128x128 (scale_a [K/128, M_total], scale_b [E] x the 128x128 grid
+    of expert e's B as stored).  bias None, values [N] (every expert) or
+    [E, N] (row e for expert e).
     Returns (out [M_total, N] float64 with NaN in rows no group owns,
     rows_written bool [M_total])."""
+    if (recipe_a, recipe_b) not in GROUPED_PAIRS:
+        raise NotImplementedError((recipe_a, recipe_b))
     A = np.asarray(A, np.uint8)
     W = np.asarray(W, np.uint8)
     M_total, K = A.shape
-    E, N, _ = W.shape
+    E = W.shape[0]
+    N = W.shape[1] if layout == "NK" else W.shape[2]
+    scale_a = np.asarray(scale_a)
     out = np.full((M_total, N), np.nan)
     written = np.zeros(M_total, bool)
     start = 0
@@ -181,12 +199,42 @@ def grouped_mm(A, W, offs, scale_a, scale_b, bias=None, out_dtype="bf16"):
         end = int(offs[e])
         if end > start:
             b = None if bias is None else (np.asarray(bias)[e] if np.ndim(bias) == 2 else bias)
-            out[start:end] = scaled_mm(A[start:end], W[e], scale_a[start:end],
-                                       "rowwise", scale_b[e], "rowwise", "NK",
+            sa = scale_a[start:end] if recipe_a == "rowwise" else scale_a[:, start:end]
+            out[start:end] = scaled_mm(A[start:end], W[e], sa, recipe_a,
+                                       np.asarray(scale_b)[e], recipe_b, layout,
                                        b, out_dtype)
             written[start:end] = True
         start = max(start, end)
     return out, written
+
+
+def grouped_grad_weight(gt_q, gt_scale, xt_q, xt_scale, offs, out_dtype="bf16"):
+    """Per-expert weight gradient grad_weight[e] = grad_output[rows_e].T @
+    input[rows_e] (the dense weight-gradient call form applied to expert e's
+    tokens), both operands in the grouped 128x1 layout of
+    ``quant.quantize_grouped_128x1``: gt_q [N_out, P] with gt_scale [NB, N_out],
+    xt_q [K_in, P] with xt_scale [NB, K_in].  The sum runs over the expert's
+    own tokens only; an expert without tokens gets zeros.
+    Returns [E, N_out, K_in] float64, rounded once to out_dtype."""
+    gt_q = np.asarray(gt_q, np.uint8)
+    xt_q = np.asarray(xt_q, np.uint8)
+    gt_scale = np.asarray(gt_scale, np.float64)
+    xt_scale = np.asarray(xt_scale, np.float64)
+    start, end, first, _ = quant.grouped_blocks(offs)
+    E = end.size
+    N_out, K_in = gt_q.shape[0], xt_q.shape[0]
+    out = np.zeros((E, N_out, K_in))
+    for e in range(E):
+        m = int(end[e] - start[e])
+        if m == 0:
+            continue
+        j = np.arange(m)
+        cols = 128 * int(first[e]) + j                   # the expert's tokens
+        blocks = int(first[e]) + j // 128                # their scaling runs
+        a = e4m3.decode(gt_q[:, cols]) * gt_scale[blocks].T     # [N_out, m]
+        b = e4m3.decode(xt_q[:, cols]) * xt_scale[blocks].T     # [K_in, m]
+        out[e] = a @ b.T
+    return round_out(out, out_dtype)
 
 
 def linear_forward(x_q, x_scale, x_recipe, w_q, w_scale, w_recipe, bias=None,

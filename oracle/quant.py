@@ -33,6 +33,9 @@ Scale layouts (float32, C order):
   block (128, 128)    [rows/128, cols/128]
   block (128, 1)      [rows/128, cols]       (codes optionally written
                                               transposed as [cols, rows])
+  grouped (128, 1)    [runs, cols]           runs of 128 tokens restarted at
+                                              each expert (see
+                                              ``quantize_grouped_128x1``)
 
 Pins: ``tests/test_oracle_quant.py`` (power-of-two round trips, the
 "amax element encodes to +-448" invariant, designed-amax layout checks, the
@@ -124,3 +127,63 @@ def dequantize(q, scale, block_rows, block_cols):
         grid = scale
     s_elem = np.repeat(np.repeat(grid, block_rows, 0), block_cols, 1)
     return vals * s_elem
+
+
+# ---------------------------------------------------------------------------
+# Grouped (MoE) weight-gradient operands: 128x1 runs that restart at each
+# expert's first token.
+#
+# The pages give the grouped GEMM only for the forward, rowwise, with expert e
+# owning activation rows [offs[e-1], offs[e]) (pytorch/ao PR #4390, "Add
+# _grouped_mm dispatch handler to Float8Tensor", "Design"), and the 128x1
+# token runs only for the dense weight gradient (pytorch/ao PR #2784, "improve
+# fp8 blockwise gemm perf", second table).  Reading for the grouped weight
+# gradient: each expert's tokens are cut into runs of 128 from the expert's
+# first token (the last run may be shorter), so no scaling group mixes two
+# experts; each run x column is one group.  The codes are stored transposed,
+# each expert starting at a multiple of 128 columns of a padded token axis:
+# run j of expert e is block first_block[e] + j, first_block being the
+# exclusive prefix sum of the experts' run counts ceil(m_e / 128); columns of
+# a short run past the expert's last token hold zero codes.
+# ---------------------------------------------------------------------------
+
+def group_ranges(offs):
+    """Row range [start, end) of every expert: [offs[e-1], offs[e]) with
+    offs[-1] = 0.  Offsets must be non-decreasing and non-negative."""
+    offs = np.asarray(offs, np.int64)
+    assert offs.ndim == 1 and (offs >= 0).all() and (np.diff(offs) >= 0).all()
+    start = np.concatenate([[0], offs[:-1]]).astype(np.int64)
+    return start, offs.copy()
+
+
+def grouped_blocks(offs):
+    """(start, end, first_block, n_blocks) per expert for the padded token
+    layout: n_blocks = ceil((end - start) / 128), first_block its exclusive
+    prefix sum."""
+    start, end = group_ranges(offs)
+    n_blocks = (end - start + 127) // 128
+    first = np.concatenate([[0], np.cumsum(n_blocks)[:-1]]).astype(np.int64)
+    return start, end, first, n_blocks
+
+
+def quantize_grouped_128x1(x_bits, offs):
+    """x bf16 bits [T, C], offs int [E] (end offsets, offs[E-1] <= T).
+    Returns (qt uint8 [C, 128 * NB], scale float32 [NB, C], first_block [E])
+    with NB the total run count; rows at or past offs[E-1] belong to no run."""
+    x = bf16_to_f32(x_bits)
+    T, C = x.shape
+    start, end, first, n_blocks = grouped_blocks(offs)
+    assert end.size == 0 or end[-1] <= T
+    NB = int(n_blocks.sum())
+    qt = np.zeros((C, 128 * NB), np.uint8)
+    scale = np.zeros((NB, C), np.float32)
+    for e in range(end.size):
+        for j in range(int(n_blocks[e])):
+            r0 = int(start[e]) + 128 * j
+            r1 = min(r0 + 128, int(end[e]))
+            run = x[r0:r1]                                   # [rows, C]
+            s = scale_from_amax(np.max(np.abs(run), axis=0))  # [C]
+            b = int(first[e]) + j
+            scale[b] = s
+            qt[:, 128 * b:128 * b + (r1 - r0)] = cast(run, s[None, :]).T
+    return qt, scale, first

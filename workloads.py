@@ -25,6 +25,9 @@ blockwise shapes are the llama4 w1/w3 and w2 GEMMs of pytorch/ao PR #2784,
   4 grouped MoE  act [16384, 2048] ~N(0,1), W [64, 1408, 2048] ~N(0, 0.02),
                  group sizes ~ multinomial(16384, uniform over 64), offsets =
                  cumulative int32 end offsets
+  5 grouped MoE backward: the tensors and routing of 4, plus grad_output
+                 [16384, 1408] ~N(0, 1e-3) (the dense weight gradient's
+                 grad_output distribution)
 Every generator takes optional smaller sizes so that the same distributions
 serve the oracle-sized parity cases.
 """
@@ -93,3 +96,10 @@ def grouped(E=64, N=1408, K=2048, M_total=16384, seed=SEED_BASE + 4):
     return {"act": normal_bf16(g[0], (M_total, K)),
             "W": normal_bf16(g[1], (E, N, K), 0.02),
             "sizes": sizes.astype(np.int64), "offs": offs}
+
+
+def grouped_backward(E=64, N=1408, K=2048, M_total=16384, seed=SEED_BASE + 5):
+    fwd = grouped(E=E, N=N, K=K, M_total=M_total)
+    g = streams(seed, 1)
+    fwd["grad_output"] = normal_bf16(g[0], (M_total, N), 1e-3)
+    return fwd
