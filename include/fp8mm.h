@@ -209,6 +209,86 @@ fp8mm_status fp8_scaled_grouped_mm(const uint8_t* A, int64_t M_total,
                                    const void* bias, fp8mm_out_dtype out_dtype,
                                    void* out, int64_t ldo, hipStream_t stream);
 
+/* Grouped (MoE) scaled GEMM with an explicit recipe per operand (the recipe
+ * table of pytorch PR #164141, "Add _scaled_mm_v2 API", applied to the
+ * grouped form of pytorch/ao PR #4390, "Add _grouped_mm dispatch handler to
+ * Float8Tensor").  Expert e multiplies rows [offsets[e-1], offsets[e]) of A
+ * by its own B_e:
+ *   A: uint8 [M_total, K] (lda = K).
+ *   B_E: uint8 [E, N, K] (B_NK: the forward's grouped_mm(act,
+ *     weight.transpose(-2, -1)) form) or [E, K, N] (B_KN: e.g. the stored
+ *     [E, N_out, K_in] expert weights read by the input gradient, which
+ *     contracts over N_out).
+ *   (ROWWISE, ROWWISE): scale_a float32 [M_total], scale_b [E, N].
+ *   (BLOCK_1x128, BLOCK_128x128): scale_a [K/128, M_total]; scale_b expert
+ *     e's 128x128 grid of B_e as stored, [E, N/128, K/128] (B_NK) or
+ *     [E, K/128, N/128] (B_KN); K % 128 == 0 and N % 128 == 0.  The pages
+ *     give the grouped GEMM only with rowwise scales; this pair is the
+ *     blockwise recipe applied per expert.
+ *   Any other pair -> FP8MM_ENOTIMPL.
+ *   B_KN: N % 16 == 0 and K * N < 2^31.
+ *   offsets, bias ([E, N] or NULL), out and the treatment of the offsets:
+ *   as fp8_scaled_grouped_mm.  K % 16 == 0. */
+fp8mm_status fp8_scaled_grouped_mm_v2(const uint8_t* A, int64_t M_total,
+                                      int64_t K, const uint8_t* B_E, int64_t E,
+                                      int64_t N, fp8mm_b_layout b_layout,
+                                      const int32_t* offsets,
+                                      const float* scale_a,
+                                      fp8mm_recipe recipe_a,
+                                      const float* scale_b,
+                                      fp8mm_recipe recipe_b, const void* bias,
+                                      fp8mm_out_dtype out_dtype, void* out,
+                                      int64_t ldo, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Grouped (MoE) weight gradient: grad_w[e] = grad_output[rows_e].t() @
+ * input[rows_e] for every expert e, the weight-gradient call form (ColossalAI
+ * PR #6419, "Backward pass"; 1x128 x 128x1 along the tokens, pytorch/ao PR
+ * #2784, second table) applied to each expert's own tokens, expert e owning
+ * token rows [offsets[e-1], offsets[e]) as in the grouped GEMM.  The pages
+ * give 128-token scaling runs only for the dense case; here the runs restart
+ * at each expert's first token, so that no scaling group mixes two experts.
+ * ------------------------------------------------------------------------- */
+
+/* Run capacity for T tokens and E experts: T/128 + E (each expert adds at
+ * most one short run); -1 for negative arguments.  Host only. */
+int64_t fp8mm_grouped_runs_capacity(int64_t T, int64_t E);
+
+/* Quantize x bf16 [T, C] (ld_x >= C, C % 16 == 0) in runs of 128 tokens per
+ * expert: each expert's rows are cut into runs of 128 from its first row
+ * (the last run may be shorter); each run x column is one scaling group,
+ * s = fl32(amax / 448) (zero amax -> 1), code = e4m3(x / s) as in
+ * fp8_quantize_blockwise.  Runs are numbered over all experts in order; run
+ * r is written transposed at columns [128 r, 128 r + 128) of q_t [C, ld_q]
+ * (zero codes in the columns past a short run's last token) with its scales
+ * at row r of scale [ld_q / 128, C].  ld_q >= 128 x fp8mm_grouped_runs_capacity
+ * (T, E) and a multiple of 16.  Columns and scale rows past the last run are
+ * not written; rows of x at or past offsets[E-1] are not read.  offsets:
+ * DEVICE int32 [E], treated as in the grouped GEMM. */
+fp8mm_status fp8_quantize_grouped_128x1(const void* x, int64_t T, int64_t C,
+                                        int64_t ld_x, const int32_t* offsets,
+                                        int64_t E, uint8_t* q_t, int64_t ld_q,
+                                        float* scale, hipStream_t stream);
+
+/* grad_w bf16 or fp32 [E, N_out, K_in] (dense) from the two quantizer
+ * outputs of the same offsets, T and ld:
+ *   gt_q uint8 [N_out, ld], gt_scale float32 [ld/128, N_out]: grad_output
+ *     [T, N_out] quantized by fp8_quantize_grouped_128x1;
+ *   xt_q uint8 [K_in, ld], xt_scale [ld/128, K_in]: input [T, K_in] likewise.
+ * Expert e contracts over its runs only, the zero codes of a short run's
+ * missing tokens included (codes there must be zero, as the quantizer writes
+ * them); an expert without tokens gets zeros.  Offsets that are not
+ * non-decreasing are undefined input; the kernel still reads only the first
+ * ld/128 runs. */
+fp8mm_status fp8_grouped_linear_grad_weight(const uint8_t* gt_q, int64_t N_out,
+                                            const float* gt_scale,
+                                            const uint8_t* xt_q, int64_t K_in,
+                                            const float* xt_scale, int64_t ld,
+                                            int64_t T, const int32_t* offsets,
+                                            int64_t E,
+                                            fp8mm_out_dtype out_dtype,
+                                            void* grad_w, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * The three call forms of an FP8 linear layer (ColossalAI PR #6419, "Forward
  * pass" and "Backward pass"; pytorch/ao PR #2784 names the blockwise GEMMs

@@ -19,7 +19,8 @@ from . import _lib
 
 __all__ = [
     "fp8_quantize_tensorwise", "fp8_quantize_rowwise", "fp8_quantize_blockwise", "fp8_quantize_blockwise_dual", "fp8_quantize_mx",
-    "fp8_scaled_mm", "fp8_scaled_grouped_mm", "fp8_linear_forward",
+    "fp8_scaled_mm", "fp8_scaled_grouped_mm", "fp8_scaled_grouped_mm_v2", "grouped_runs_capacity",
+    "fp8_quantize_grouped_128x1", "fp8_grouped_linear_grad_weight", "fp8_linear_forward",
     "fp8_linear_grad_input", "fp8_linear_grad_weight", "recipe_pair_supported",
     "FP8BlockwiseLinear", "fp8_blockwise_linear",
 ]
@@ -236,6 +237,108 @@ def fp8_scaled_grouped_mm(A, B_EnK, offsets, scale_a, scale_b, bias=None, out_dt
                                            scale_a.data_ptr(), scale_b.data_ptr(), _ptr(bias),
                                            _out_code(out_dtype), out.data_ptr(), _ld(out, "out"), _stream(A))
     _lib.check(st, "fp8_scaled_grouped_mm")
+    return out
+
+
+def fp8_scaled_grouped_mm_v2(A, B_E, offsets, scale_a, recipe_a, scale_b, recipe_b, b_layout="NK", bias=None,
+                             out_dtype=torch.bfloat16, out=None):
+    """Grouped (MoE) GEMM with explicit recipes: rows [offsets[e-1],
+    offsets[e]) of A [M_total, K] times expert e's B, B_E uint8 [E, N, K]
+    (b_layout "NK") or [E, K, N] ("KN").  Pairs: rowwise x rowwise (scale_a
+    [M_total], scale_b [E, N]) and 1x128 x 128x128 (scale_a [K/128, M_total],
+    scale_b [E] x expert e's 128x128 grid of B as stored).  Rows at or past
+    offsets[-1] are left as they are in `out` (zeros when allocated here)."""
+    if offsets is None:
+        raise ValueError("offsets are required for the grouped GEMM")
+    if b_layout not in _lib.B_LAYOUTS:
+        raise ValueError(f"b_layout must be 'NK' or 'KN', got {b_layout!r}")
+    _need(A, torch.uint8, "A")
+    _need(B_E, torch.uint8, "B_E")
+    _need(offsets, torch.int32, "offsets")
+    if B_E.dim() != 3 or not B_E.is_contiguous() or A.dim() != 2 or not A.is_contiguous():
+        raise ValueError("A must be contiguous [M_total, K] and B_E contiguous 3-D")
+    M, K = A.shape
+    if b_layout == "NK":
+        E, N, K2 = B_E.shape
+    else:
+        E, K2, N = B_E.shape
+    if K2 != K:
+        raise ValueError(f"contraction mismatch: A has K={K}, B_E has {K2}")
+    if offsets.numel() != E or not offsets.is_contiguous():
+        raise ValueError("offsets must be a contiguous int32 tensor of E elements")
+    ra, rb = _recipe(recipe_a), _recipe(recipe_b)
+    for t, n in ((scale_a, "scale_a"), (scale_b, "scale_b")):
+        _need(t, torch.float32, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if (ra, rb) == (_lib.RECIPES["1x128"], _lib.RECIPES["128x128"]):
+        want_a, want_b = (K // 128) * M, E * (N // 128) * (K // 128)
+    else:
+        want_a, want_b = M, E * N
+    if scale_a.numel() != want_a or scale_b.numel() != want_b:
+        raise ValueError(f"scales have {scale_a.numel()} and {scale_b.numel()} elements, "
+                         f"the recipes need {want_a} and {want_b}")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias")
+        if bias.numel() != E * N or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous bf16 [E, N] tensor")
+    if out is None:
+        out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
+    st = _lib.load().fp8_scaled_grouped_mm_v2(A.data_ptr(), M, K, B_E.data_ptr(), E, N, _lib.B_LAYOUTS[b_layout],
+                                              offsets.data_ptr(), scale_a.data_ptr(), ra, scale_b.data_ptr(), rb,
+                                              _ptr(bias), _out_code(out_dtype), out.data_ptr(), _ld(out, "out"),
+                                              _stream(A))
+    _lib.check(st, "fp8_scaled_grouped_mm_v2")
+    return out
+
+
+def grouped_runs_capacity(T, E):
+    """Runs of 128 tokens that T tokens over E experts can need: T // 128 + E."""
+    return int(_lib.load().fp8mm_grouped_runs_capacity(int(T), int(E)))
+
+
+def fp8_quantize_grouped_128x1(x, offsets):
+    """x bf16 [T, C] -> (q_t uint8 [C, ld], scale float32 [ld / 128, C]) with
+    ld = 128 * grouped_runs_capacity(T, E): runs of 128 tokens restarted at
+    each expert's first token (offsets int32 [E], cumulative end rows), run r
+    at columns [128 r, 128 r + 128).  Columns and scale rows past the last run
+    are left unwritten."""
+    _need(x, torch.bfloat16, "x")
+    _need(offsets, torch.int32, "offsets")
+    if not offsets.is_contiguous() or offsets.dim() != 1:
+        raise ValueError("offsets must be a contiguous 1-D int32 tensor")
+    T, C = x.shape
+    E = offsets.numel()
+    ld = 128 * grouped_runs_capacity(T, E)
+    q = torch.empty((C, max(ld, 16)), dtype=torch.uint8, device=x.device)
+    scale = torch.empty((ld // 128, C), dtype=torch.float32, device=x.device)
+    st = _lib.load().fp8_quantize_grouped_128x1(x.data_ptr(), T, C, _ld(x, "x"), offsets.data_ptr(), E,
+                                                q.data_ptr(), q.stride(0), scale.data_ptr(), _stream(x))
+    _lib.check(st, "fp8_quantize_grouped_128x1")
+    return q, scale
+
+
+def fp8_grouped_linear_grad_weight(gt_q, gt_scale, xt_q, xt_scale, offsets, T, out_dtype=torch.bfloat16):
+    """grad_w [E, N_out, K_in]: expert e's grad_output[rows_e].t() @
+    input[rows_e] from the two outputs of fp8_quantize_grouped_128x1 with the
+    same offsets and token count T."""
+    for t, n in ((gt_q, "gt_q"), (xt_q, "xt_q")):
+        _need(t, torch.uint8, n)
+    for t, n in ((gt_scale, "gt_scale"), (xt_scale, "xt_scale")):
+        _need(t, torch.float32, n)
+    _need(offsets, torch.int32, "offsets")
+    N_out, ld = gt_q.shape
+    K_in = xt_q.shape[0]
+    E = offsets.numel()
+    if xt_q.shape[1] != ld or not (gt_q.is_contiguous() and xt_q.is_contiguous()):
+        raise ValueError("gt_q [N_out, ld] and xt_q [K_in, ld] must be contiguous with the same ld")
+    if gt_scale.shape != (ld // 128, N_out) or xt_scale.shape != (ld // 128, K_in):
+        raise ValueError("scales must be [ld/128, N_out] and [ld/128, K_in]")
+    out = torch.empty((E, N_out, K_in), dtype=out_dtype, device=gt_q.device)
+    st = _lib.load().fp8_grouped_linear_grad_weight(gt_q.data_ptr(), N_out, gt_scale.data_ptr(), xt_q.data_ptr(),
+                                                    K_in, xt_scale.data_ptr(), ld, int(T), offsets.data_ptr(), E,
+                                                    _out_code(out_dtype), out.data_ptr(), _stream(gt_q))
+    _lib.check(st, "fp8_grouped_linear_grad_weight")
     return out
 
 

@@ -271,6 +271,128 @@ fp8mm_status fp8_scaled_grouped_mm(const uint8_t* A, int64_t M_total, int64_t K,
   return from_hip(fp8mm::launch_gemm(p, stream), "fp8_scaled_grouped_mm");
 }
 
+fp8mm_status fp8_scaled_grouped_mm_v2(const uint8_t* A, int64_t M_total, int64_t K, const uint8_t* B_E, int64_t E,
+                                      int64_t N, fp8mm_b_layout b_layout, const int32_t* offsets,
+                                      const float* scale_a, fp8mm_recipe recipe_a, const float* scale_b,
+                                      fp8mm_recipe recipe_b, const void* bias, fp8mm_out_dtype out_dtype, void* out,
+                                      int64_t ldo, hipStream_t stream) {
+  if (!valid_recipe(recipe_a) || !valid_recipe(recipe_b)) return fail(FP8MM_EINVAL, "unknown recipe value");
+  if (b_layout != FP8MM_B_NK && b_layout != FP8MM_B_KN) return fail(FP8MM_EINVAL, "unknown B layout");
+  if (!offsets) return fail(FP8MM_EINVAL, "offsets are required for the grouped GEMM");
+  if (out_dtype != FP8MM_OUT_BF16 && out_dtype != FP8MM_OUT_FP32) return fail(FP8MM_EINVAL, "unknown out_dtype");
+  if (M_total < 0 || K < 0 || N < 0 || E < 0) return fail(FP8MM_EINVAL, "negative shape");
+  if (M_total > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1 || E > (int64_t(1) << 20))
+    return fail(FP8MM_EINVAL, "M_total and N must be < 2^31 and E <= 2^20");
+  fp8mm::Epi epi;
+  if (recipe_a == FP8MM_ROWWISE && recipe_b == FP8MM_ROWWISE)
+    epi = fp8mm::Epi::Row;
+  else if (recipe_a == FP8MM_BLOCK_1x128 && recipe_b == FP8MM_BLOCK_128x128)
+    epi = fp8mm::Epi::Block128x128;
+  else
+    return fail(FP8MM_ENOTIMPL, "grouped recipe pair (%d, %d) is not implemented (rowwise x rowwise or "
+                "1x128 x 128x128)", int(recipe_a), int(recipe_b));
+  if (K % 16 != 0 || K > kMaxLd) return fail(FP8MM_EINVAL, "K (%lld) must be a multiple of 16 and <= 2^22", (long long)K);
+  if (epi == fp8mm::Epi::Block128x128 && (K % 128 != 0 || N % 128 != 0))
+    return fail(FP8MM_EINVAL, "1x128 x 128x128 needs K %% 128 == 0 and N %% 128 == 0 (K=%lld N=%lld)", (long long)K,
+                (long long)N);
+  if (b_layout == FP8MM_B_KN) {
+    if (N % 16 != 0 || N > kMaxLd) return fail(FP8MM_EINVAL, "B stored [K, N] needs N %% 16 == 0 and N <= 2^22");
+    if (K * N > (int64_t(1) << 31)) return fail(FP8MM_EINVAL, "each expert's B stored [K, N] must span fewer than 2^31 bytes");
+  }
+  if (ldo < N) return fail(FP8MM_EINVAL, "ldo (%lld) must be >= N (%lld)", (long long)ldo, (long long)N);
+  if (M_total == 0 || N == 0 || E == 0) return ok();
+  if (!scale_a || !scale_b || !out) return fail(FP8MM_EINVAL, "null pointer argument (scales and out are required)");
+  if (K > 0 && (!A || !B_E)) return fail(FP8MM_EINVAL, "null pointer argument (A and B_E are required when K > 0)");
+  if (!aligned16(A) || !aligned16(B_E)) return fail(FP8MM_EINVAL, "A and B_E must be 16-byte aligned");
+  fp8mm::GemmProblem p{};
+  p.A = A;
+  p.B = B_E;
+  p.sa = scale_a;
+  p.sb = scale_b;
+  p.bias = static_cast<const uint16_t*>(bias);
+  p.out = out;
+  p.M = M_total;
+  p.N = N;
+  p.K = K;
+  p.lda = K;
+  p.ldb = b_layout == FP8MM_B_NK ? K : N;
+  p.ldo = ldo;
+  p.epi = epi;
+  p.b_kn = b_layout == FP8MM_B_KN;
+  p.out_bf16 = out_dtype == FP8MM_OUT_BF16;
+  p.offsets = offsets;
+  p.E = E;
+  p.row_begin = 0;
+  p.row_end = M_total;
+  return from_hip(fp8mm::launch_gemm(p, stream), "fp8_scaled_grouped_mm_v2");
+}
+
+int64_t fp8mm_grouped_runs_capacity(int64_t T, int64_t E) {
+  if (T < 0 || E < 0) return -1;
+  return T / 128 + E;
+}
+
+fp8mm_status fp8_quantize_grouped_128x1(const void* x, int64_t T, int64_t C, int64_t ld_x, const int32_t* offsets,
+                                        int64_t E, uint8_t* q_t, int64_t ld_q, float* scale, hipStream_t stream) {
+  fp8mm_status st = check_quant_common(x, T, C, ld_x, q_t, scale);
+  if (st != FP8MM_OK) return st;
+  if (E < 0 || E > (int64_t(1) << 20)) return fail(FP8MM_EINVAL, "E (%lld) must be in [0, 2^20]", (long long)E);
+  if (!offsets && E > 0) return fail(FP8MM_EINVAL, "offsets are required");
+  const int64_t runs = T / 128 + E;
+  if (ld_q < 128 * runs || ld_q % 16 != 0 || ld_q > kMaxLd)
+    return fail(FP8MM_EINVAL, "ld_q (%lld) must be >= 128 (T/128 + E) = %lld, a multiple of 16 and <= 2^22",
+                (long long)ld_q, (long long)(128 * runs));
+  if (C / 128 + 1 > 65535) return fail(FP8MM_EINVAL, "C (%lld) must be below 128 x 65535", (long long)C);
+  if (T == 0 || C == 0 || E == 0) return ok();
+  if (!scale) return fail(FP8MM_EINVAL, "scale must not be NULL");
+  return from_hip(fp8mm::launch_quant_grouped_128x1(static_cast<const uint16_t*>(x), T, C, ld_x, offsets, E, q_t,
+                                                    ld_q, scale, stream),
+                  "fp8_quantize_grouped_128x1");
+}
+
+fp8mm_status fp8_grouped_linear_grad_weight(const uint8_t* gt_q, int64_t N_out, const float* gt_scale,
+                                            const uint8_t* xt_q, int64_t K_in, const float* xt_scale, int64_t ld,
+                                            int64_t T, const int32_t* offsets, int64_t E, fp8mm_out_dtype out_dtype,
+                                            void* grad_w, hipStream_t stream) {
+  if (out_dtype != FP8MM_OUT_BF16 && out_dtype != FP8MM_OUT_FP32) return fail(FP8MM_EINVAL, "unknown out_dtype");
+  if (N_out < 0 || K_in < 0 || T < 0 || E < 0) return fail(FP8MM_EINVAL, "negative shape");
+  if (N_out > (int64_t(1) << 31) - 1 || K_in > (int64_t(1) << 31) - 1 || E > (int64_t(1) << 20))
+    return fail(FP8MM_EINVAL, "N_out and K_in must be < 2^31 and E <= 2^20");
+  if (!offsets && E > 0) return fail(FP8MM_EINVAL, "offsets are required");
+  const int64_t runs = T / 128 + E;
+  if (ld < 128 * runs || ld % 16 != 0 || ld > kMaxLd)
+    return fail(FP8MM_EINVAL, "ld (%lld) must be >= 128 (T/128 + E) = %lld, a multiple of 16 and <= 2^22",
+                (long long)ld, (long long)(128 * runs));
+  if (N_out == 0 || K_in == 0 || E == 0) return ok();
+  const int64_t tiles = ((N_out + 127) / 128) * ((K_in + 127) / 128) * E;
+  if (tiles > (int64_t(1) << 31) - 8) return fail(FP8MM_EINVAL, "too many output tiles");
+  if (!gt_q || !xt_q || !gt_scale || !xt_scale || !grad_w) return fail(FP8MM_EINVAL, "null pointer argument");
+  if (!aligned16(gt_q) || !aligned16(xt_q)) return fail(FP8MM_EINVAL, "gt_q and xt_q must be 16-byte aligned");
+  fp8mm::GemmProblem p{};
+  p.A = gt_q;
+  p.B = xt_q;
+  p.sa = gt_scale;
+  p.sb = xt_scale;
+  p.bias = nullptr;
+  p.out = grad_w;
+  p.M = N_out;
+  p.N = K_in;
+  p.K = 0;
+  p.lda = ld;
+  p.ldb = ld;
+  p.ldo = K_in;
+  p.epi = fp8mm::Epi::Block128x1;
+  p.b_kn = false;
+  p.out_bf16 = out_dtype == FP8MM_OUT_BF16;
+  p.offsets = offsets;
+  p.E = E;
+  p.row_begin = 0;
+  p.row_end = N_out;
+  p.group_k = true;
+  p.tokens = T;
+  return from_hip(fp8mm::launch_gemm(p, stream), "fp8_grouped_linear_grad_weight");
+}
+
 // ------------------------------------------------------------- call forms
 
 fp8mm_status fp8_linear_forward(const uint8_t* x_q, int64_t M, int64_t K, const float* x_scale,

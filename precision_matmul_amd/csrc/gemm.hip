@@ -61,9 +61,13 @@ __device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t c[4])
   c[3] = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
 }
 
+// GROUPED_K: the grouped weight gradient, E problems of M x N that contract
+// over the experts' runs of 128 tokens (offsets along K); two workgroups per
+// CU, so that one's epilogue overlaps the other's loads.
 template <int BM, int BN, int WM, int WN, int STAGES, Epi EPI, bool B_KN, bool OUT_BF16, bool BIAS, bool GROUPED,
-          bool K_ALIGNED>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n, int vec_out) {
+          bool K_ALIGNED, bool GROUPED_K = false>
+__global__ __launch_bounds__(WM * WN * 64, GROUPED_K ? 2 : 1) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n,
+                                                                              int vec_out) {
   constexpr int NW = WM * WN;            // waves: WM along M x WN along N
   constexpr int NT = NW * 64;
   constexpr int TM = BM / WM;
@@ -76,6 +80,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
   // the blockwise scales and applied by the block-scaled MFMA.
   constexpr bool MX = EPI == Epi::MX;
   static_assert(!MX || (!B_KN && !GROUPED), "MXFP8: plain GEMMs with B stored [N, K]");
+  static_assert(!GROUPED || EPI == Epi::Row || EPI == Epi::Block128x128, "grouped: rowwise or 1x128 x 128x128");
+  static_assert(!GROUPED_K || (EPI == Epi::Block128x1 && !B_KN && !GROUPED && !BIAS), "grouped weight gradient");
   constexpr int A_BYTES = BM * BK;
   constexpr int B_BYTES = BN * BK;
   // Scale regions (blockwise): 8 chunks of 256 bytes, 4 for sA (BM = 256
@@ -120,7 +126,42 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
 
   // ---------------- tile selection ----------------
   TileInfo ti;
-  if constexpr (!GROUPED) {
+  ti.sa = p.sa;
+  ti.K = int(p.K);
+  ti.out_off = 0;
+  if constexpr (GROUPED_K) {
+    // Expert e = lin / (tiles_m tiles_n): one expert's tiles are consecutive
+    // in one XCD, whose L2 then holds that expert's operand columns.  Its
+    // operands are the columns [128 first, 128 (first + runs)) of the padded
+    // token axis, its scales rows [first, first + runs) of [runs, M] and
+    // [runs, N], its output problem e of [E, M, N].
+    const int64_t per_xcd = gridDim.x / 8;   // the launcher pads the grid to a multiple of 8
+    const int64_t lin = int64_t(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    const int64_t tiles = int64_t(tiles_m) * tiles_n;
+    const int64_t e = lin / tiles;
+    if (e >= p.E) return;
+    const int t = int(lin - e * tiles);
+    const int tm = t / tiles_n, tn = t % tiles_n;
+    int64_t first = 0;
+    int runs = 0;
+    grp::runs_before(p.offsets, p.tokens, 128, e, first, runs);
+    // the operands and scales hold lda / 128 runs; offsets that are not
+    // non-decreasing could ask for more, which are dropped
+    const int64_t cap = p.lda / 128;
+    first = min(first, cap);
+    runs = int(min<int64_t>(runs, cap - first));
+    ti.row0 = int64_t(tm) * BM;
+    ti.rows_valid = int(min<int64_t>(BM, p.M - ti.row0));
+    ti.n0 = int64_t(tn) * BN;
+    ti.cols_valid = int(min<int64_t>(BN, p.N - ti.n0));
+    ti.A = p.A + ti.row0 * p.lda + first * 128;
+    ti.B = p.B + ti.n0 * p.ldb + first * 128;
+    ti.sa = p.sa + first * p.M;
+    ti.sb = p.sb + first * p.N;
+    ti.bias = nullptr;
+    ti.K = runs * 128;
+    ti.out_off = e * p.M * p.ldo;
+  } else if constexpr (!GROUPED) {
     int tm, tn;
     if (!tile_coords(tiles_m, tiles_n, tm, tn)) return;
     ti.row0 = p.row_begin + int64_t(tm) * BM;
@@ -145,12 +186,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
     ti.n0 = int64_t(tn) * BN;
     ti.cols_valid = int(min<int64_t>(BN, p.N - ti.n0));
     ti.A = p.A + ti.row0 * p.lda;
-    ti.B = p.B + int64_t(e_found) * p.N * p.K + ti.n0 * p.ldb;
-    ti.sb = p.sb + int64_t(e_found) * p.N;
+    // expert e: B [N, K] or [K, N] at B + e N K; scales row e of [E, N]
+    // (rowwise) or grid e of [E, N/128 x K/128] (128x128)
+    ti.B = p.B + int64_t(e_found) * p.N * p.K + (B_KN ? ti.n0 : ti.n0 * p.ldb);
+    ti.sb = p.sb + int64_t(e_found) * (EPI == Epi::Block128x128 ? (p.N / 128) * (p.K / 128) : p.N);
     ti.bias = BIAS ? p.bias + int64_t(e_found) * p.N : nullptr;
   }
 
-  const int K = int(p.K);
+  const int K = ti.K;
   const int nk = (K + BK - 1) / BK;
   // Split K: grid row y covers K steps [kt_begin, kt_end) (all of K when the
   // grid has one row).
@@ -210,7 +253,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
       const int64_t first = (c < 4 ? ti.row0 : ti.n0) + 64 * w4;
       const int valid = c < 4 ? ti.rows_valid : ti.cols_valid;
       const int here = live ? min(max(valid - 64 * w4, 0), 64) : 0;
-      const uint8_t* base = (c < 4 ? reinterpret_cast<const uint8_t*>(p.sa) : reinterpret_cast<const uint8_t*>(ti.sb)) +
+      const uint8_t* base = (c < 4 ? reinterpret_cast<const uint8_t*>(ti.sa) : reinterpret_cast<const uint8_t*>(ti.sb)) +
                             (here > 0 ? first * nkb : 0);
       const Rsrc r = make_rsrc4(base, uint32_t(here) * uint32_t(nkb));
       dma_b32(r, st + A_BYTES + B_BYTES + (c < 4 ? 0 : SA_BYTES) + w4 * 256,
@@ -223,7 +266,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
         // edge read neighbouring scales that only reach rows never stored.
         const int64_t off = int64_t(kt) * p.M + ti.row0 + c * 64;
         const int64_t rem = int64_t(nk) * p.M - off;
-        const Rsrc r = make_rsrc4(p.sa + (rem > 0 ? off : 0), uint32_t(rem > 0 && live ? rem * 4 : 0));
+        const Rsrc r = make_rsrc4(ti.sa + (rem > 0 ? off : 0), uint32_t(rem > 0 && live ? rem * 4 : 0));
         dma_b32(r, st + A_BYTES + B_BYTES + c * 256, uint32_t(lane) * 4u);
       } else {
         const int cc = c - 4;
@@ -499,7 +542,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmProblem p, in
       if (rt >= ti.rows_valid || ct >= ti.cols_valid) continue;
       const uint8_t* src = ep + rl * EPI_PITCH + ch * 16;
       uint8_t* dst = reinterpret_cast<uint8_t*>(p.out) +
-                     ((int64_t(blockIdx.y) * p.split_stride + (ti.row0 - p.out_row0 + rt) * p.ldo + ti.n0 + ct) * OUTB);
+                     ((ti.out_off + int64_t(blockIdx.y) * p.split_stride + (ti.row0 - p.out_row0 + rt) * p.ldo +
+                       ti.n0 + ct) * OUTB);
       if (vec_out && ct + EPR <= ti.cols_valid) {
         *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
       } else {
@@ -546,7 +590,7 @@ hipError_t launch_epi(const GemmProblem& p, hipStream_t st) {
   // 256 x 128 tiles, 4 waves, 3 stages; grouped: 128 x 128 tiles, 3 stages.
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
   if constexpr (GROUPED)
-    return launch_cfg<128, 128, 2, 2, 3, EPI, false, OUT_BF16, BIAS, true>(p, st);
+    return launch_cfg<128, 128, 2, 2, 3, EPI, B_KN, OUT_BF16, BIAS, true>(p, st);
   else if constexpr (BLOCKWISE && B_KN)
     return launch_cfg<256, 128, 2, 2, 3, EPI, true, OUT_BF16, BIAS, false>(p, st);   // cfg:kn_block
   else if constexpr (B_KN)
@@ -563,6 +607,24 @@ hipError_t launch_out(const GemmProblem& p, hipStream_t st) {
   if (p.out_bf16)
     return bias ? launch_epi<EPI, B_KN, true, true, GROUPED>(p, st) : launch_epi<EPI, B_KN, true, false, GROUPED>(p, st);
   return bias ? launch_epi<EPI, B_KN, false, true, GROUPED>(p, st) : launch_epi<EPI, B_KN, false, false, GROUPED>(p, st);
+}
+
+// The grouped weight gradient: 128 x 128 tiles of E problems, 2 stages (two
+// workgroups per CU), grid E x tiles padded to a multiple of 8.
+template <bool OUT_BF16>
+hipError_t launch_group_k(const GemmProblem& p, hipStream_t st) {
+  constexpr int BM = 128, BN = 128;
+  const int tiles_m = int((p.M + BM - 1) / BM), tiles_n = int((p.N + BN - 1) / BN);
+  const int64_t total = int64_t(tiles_m) * tiles_n * p.E;
+  if (total == 0) return hipSuccess;
+  const int64_t grid = (total + 7) / 8 * 8;
+  if (grid > int64_t(INT32_MAX)) return hipErrorInvalidValue;
+  const int outb = OUT_BF16 ? 2 : 4;
+  const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
+  hipLaunchKernelGGL(
+      (gemm_kernel<BM, BN, 2, 2, 2, Epi::Block128x1, false, OUT_BF16, false, false, true, true>),
+      dim3(unsigned(grid)), dim3(256), 0, st, p, tiles_m, tiles_n, vec_out);
+  return hipGetLastError();
 }
 
 // Compute units of the current device (cached per device).
@@ -690,11 +752,20 @@ hipError_t launch_tail_splitk(const GemmProblem& p, int splits, float* scratch, 
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
+  if (p.group_k) {
+    if (p.epi != Epi::Block128x1 || p.b_kn || p.bias || !p.offsets) return hipErrorInvalidValue;
+    return p.out_bf16 ? launch_group_k<true>(p, st) : launch_group_k<false>(p, st);
+  }
   if (p.offsets) {
     // grouped: the streaming kernel when its grouped loads fit the leading
-    // dimensions (K of at least 128 bytes), else 128 x 128 tiles
-    if (p.lda >= 128 && p.ldb >= 128) return launch_gemm_streaming(p, st);
-    return launch_out<Epi::Row, false, true>(p, st);
+    // dimensions (as below), else 128 x 128 tiles
+    if (p.lda >= 128 && (p.b_kn ? p.ldb >= 256 : p.ldb >= 128)) return launch_gemm_streaming(p, st);
+    if (p.epi == Epi::Row)
+      return p.b_kn ? launch_out<Epi::Row, true, true>(p, st) : launch_out<Epi::Row, false, true>(p, st);
+    if (p.epi == Epi::Block128x128)
+      return p.b_kn ? launch_out<Epi::Block128x128, true, true>(p, st)
+                    : launch_out<Epi::Block128x128, false, true>(p, st);
+    return hipErrorInvalidValue;
   }
   // The streaming kernel's grouped loads need leading dimensions of at least
   // 128 bytes (256 for B stored [K, N]).  Its 256 x 256 tiles are handed out in rounds of one per CU;

@@ -4,6 +4,7 @@
 
 #include <stdint.h>
 
+#include "grouped.hpp"
 #include "launch.hpp"
 
 namespace fp8mm {
@@ -113,6 +114,9 @@ struct TileInfo {
   const uint8_t* B;   // tile origin of B (n0 applied)
   const float* sb;    // scale_b of this problem (expert applied)
   const uint16_t* bias;
+  const float* sa;    // scale_a of this problem (grouped weight gradient: expert applied)
+  int K;              // contraction length of the tile
+  int64_t out_off;    // element offset of the tile's problem in the output
 };
 
 constexpr int epi_passes(int nw, int tm, int tn, int outb, int stage) {
@@ -143,41 +147,10 @@ __device__ __forceinline__ bool tile_coords(int tiles_m, int tiles_n, int& tm, i
 
 // Grouped problems: m-tile g, counted over all experts in expert order
 // (expert e has ceil(rows_e / bm) of them), -> expert, first row, end row.
-// Expert e owns rows [offs[e-1], offs[e]) (offs[-1] = 0), each offset
-// clamped to [0, M]; a decreasing pair is an empty group.  The whole wave
-// scans 64 experts at a time with a prefix sum of tile counts; every lane
-// gets the same answer.  Returns false when g is past the last m-tile.
+// Returns false when g is past the last m-tile.
 __device__ inline bool grouped_mtile(const GemmProblem& p, int bm, int g, int& e_out, int64_t& row0,
                                      int64_t& row_end) {
-  const int lane = threadIdx.x & 63;
-  int base = 0;
-  for (int64_t e0 = 0; e0 < p.E; e0 += 64) {
-    const int64_t e = e0 + lane;
-    int64_t start = 0, end = 0;
-    if (e < p.E) {
-      end = min<int64_t>(max<int64_t>(p.offsets[e], 0), p.M);
-      start = e == 0 ? 0 : min<int64_t>(max<int64_t>(p.offsets[e - 1], 0), p.M);
-    }
-    const int cnt = end > start ? int((end - start + bm - 1) / bm) : 0;
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
-    const bool hit = (base + incl > g) && (base + incl - cnt <= g) && cnt > 0;
-    const unsigned long long mask = __ballot(hit);
-    if (mask) {
-      const int src = __builtin_ctzll(mask);
-      const int excl = __shfl(incl - cnt, src, 64);
-      e_out = int(e0) + src;
-      row0 = __shfl(start, src, 64) + int64_t(g - base - excl) * bm;
-      row_end = __shfl(end, src, 64);
-      return true;
-    }
-    base += __shfl(incl, 63, 64);
-  }
-  return false;
+  return grp::find_run(p.offsets, p.E, p.M, bm, g, e_out, row0, row_end);
 }
 
 }  // namespace gk

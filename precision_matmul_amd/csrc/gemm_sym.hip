@@ -87,6 +87,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   // 2g + 1, in the fragment order below.
   constexpr bool MX = EPI == Epi::MX;
   static_assert(!MX || (!B_KN && !GROUPED), "MXFP8: plain GEMMs with B stored [N, K]");
+  static_assert(!GROUPED || EPI == Epi::Row || EPI == Epi::Block128x128, "grouped: rowwise or 1x128 x 128x128");
   using Fac = std::conditional_t<SWAP, float, v4f>;
   constexpr int OUTB = OUT_BF16 ? 2 : 4;
   constexpr int EPI_PASSES = epi_passes(SY_NW, SY_TM, SY_TN, OUTB, SY_STAGE);
@@ -108,7 +109,9 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   // XCDs round-robin), b / 8 = (g / 8) tiles_n + tn: the n-tiles of one
   // m-tile share its A rows in one XCD's L2, and the real m-tiles (a prefix
   // of the upper bound the grid is sized for) are spread over all XCDs.
-  // Expert e's B is [N, K] at B + e N K, its scales and bias rows e of [E, N].
+  // Expert e's B is [N, K] (or [K, N]) at B + e N K, its bias row e of
+  // [E, N], its scales row e of [E, N] (rowwise) or grid e of [E, N/128 x
+  // K/128] (128x128).
   int tn;
   int64_t row0;
   int rows_valid;
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     if (!grouped_mtile(p, SY_BM, g, e, row0, rend)) return;
     rows_valid = int(min<int64_t>(SY_BM, rend - row0));
     Bg = p.B + int64_t(e) * p.N * p.K;
-    sbg = p.sb + int64_t(e) * p.N;
+    sbg = p.sb + int64_t(e) * (EPI == Epi::Block128x128 ? (p.N / 128) * (p.K / 128) : p.N);
     if constexpr (BIAS) biasg = p.bias + int64_t(e) * p.N;
   } else {
     int tm;
@@ -655,13 +658,19 @@ hipError_t launch_sym(const GemmProblem& p, hipStream_t st) {
 template <Epi EPI>
 hipError_t launch_sym_out(const GemmProblem& p, hipStream_t st) {
   const bool bias = p.bias != nullptr;
-  if constexpr (EPI == Epi::Row) {
+  if constexpr (EPI == Epi::Row || EPI == Epi::Block128x128) {
     if (p.offsets) {
+      if (p.b_kn) {
+        if (p.out_bf16)
+          return bias ? launch_sym<EPI, true, true, true, true>(p, st) : launch_sym<EPI, true, false, true, true>(p, st);
+        return bias ? launch_sym<EPI, false, true, true, true>(p, st) : launch_sym<EPI, false, false, true, true>(p, st);
+      }
       if (p.out_bf16)
         return bias ? launch_sym<EPI, true, true, false, true>(p, st) : launch_sym<EPI, true, false, false, true>(p, st);
       return bias ? launch_sym<EPI, false, true, false, true>(p, st) : launch_sym<EPI, false, false, false, true>(p, st);
     }
   }
+  if (p.offsets) return hipErrorInvalidValue;
   if constexpr (EPI != Epi::MX) {
     if (p.b_kn) {
       if (p.out_bf16)
@@ -677,7 +686,7 @@ hipError_t launch_sym_out(const GemmProblem& p, hipStream_t st) {
 }  // namespace
 
 // Streaming schedule: plain GEMMs (B stored [N, K] or [K, N]) and grouped
-// rowwise GEMMs (expert weights [E, N, K]).
+// rowwise or 1x128 x 128x128 GEMMs (expert weights [E, N, K] or [E, K, N]).
 hipError_t launch_gemm_streaming(const GemmProblem& p, hipStream_t st) {
   switch (p.epi) {
     case Epi::Tensor: return launch_sym_out<Epi::Tensor>(p, st);

@@ -1,0 +1,86 @@
+// Expert ranges of grouped (MoE) problems, read from device offsets by the
+// grouped GEMMs and the grouped quantizer.
+//
+// Expert e owns rows [offs[e-1], offs[e]) (offs[-1] = 0) of the token axis
+// (the grouped form of pytorch/ao PR #4390, "Add _grouped_mm dispatch handler
+// to Float8Tensor", "Design"); each offset is clamped to [0, rows] and a
+// decreasing pair is an empty group.  Counts of runs of bm rows per expert
+// (ceil(rows_e / bm)) place the experts' runs one after another: the m-tiles
+// of the grouped GEMM, and the 128-token runs of the padded token axis of the
+// grouped weight gradient.  Every function is called by a whole wave, which
+// scans 64 experts at a time; all lanes get the same answer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8mm {
+namespace grp {
+
+__device__ __forceinline__ void expert_range(const int32_t* offs, int64_t rows, int64_t e, int64_t& start,
+                                             int64_t& end) {
+  end = min<int64_t>(max<int64_t>(offs[e], 0), rows);
+  start = e == 0 ? 0 : min<int64_t>(max<int64_t>(offs[e - 1], 0), rows);
+}
+
+__device__ __forceinline__ int runs_of(int64_t start, int64_t end, int bm) {
+  return end > start ? int((end - start + bm - 1) / bm) : 0;
+}
+
+// Run g, counted over all experts in expert order -> expert, first row, end
+// row of the expert.  Returns false when g is past the last run.
+__device__ inline bool find_run(const int32_t* offs, int64_t E, int64_t rows, int bm, int g, int& e_out,
+                                int64_t& row0, int64_t& row_end) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int64_t e0 = 0; e0 < E; e0 += 64) {
+    const int64_t e = e0 + lane;
+    int64_t start = 0, end = 0;
+    if (e < E) expert_range(offs, rows, e, start, end);
+    const int cnt = runs_of(start, end, bm);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    const bool hit = (base + incl > g) && (base + incl - cnt <= g) && cnt > 0;
+    const unsigned long long mask = __ballot(hit);
+    if (mask) {
+      const int src = __builtin_ctzll(mask);
+      const int excl = __shfl(incl - cnt, src, 64);
+      e_out = int(e0) + src;
+      row0 = __shfl(start, src, 64) + int64_t(g - base - excl) * bm;
+      row_end = __shfl(end, src, 64);
+      return true;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  return false;
+}
+
+// Runs of bm rows of the experts before e (first) and of expert e (count).
+__device__ inline void runs_before(const int32_t* offs, int64_t rows, int bm, int64_t e, int64_t& first,
+                                   int& count) {
+  const int lane = threadIdx.x & 63;
+  int64_t acc = 0;
+  for (int64_t e0 = 0; e0 < e; e0 += 64) {
+    const int64_t ee = e0 + lane;
+    if (ee < e) {
+      int64_t start, end;
+      expert_range(offs, rows, ee, start, end);
+      acc += runs_of(start, end, bm);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  // every lane holds the sum: make it visibly wave-uniform (scalar registers)
+  first = int64_t((uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(acc >> 32)))) << 32) |
+                  uint32_t(__builtin_amdgcn_readfirstlane(int(acc))));
+  int64_t start, end;
+  expert_range(offs, rows, e, start, end);
+  count = runs_of(start, end, bm);
+}
+
+}  // namespace grp
+}  // namespace fp8mm

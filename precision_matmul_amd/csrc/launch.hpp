@@ -23,6 +23,15 @@ hipError_t launch_quant_blockwise_dual(const uint16_t* x, int64_t rows, int64_t 
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
                            uint8_t* scale, hipStream_t st);
 
+// Grouped 128x1 quantization for the grouped weight gradient: runs of 128
+// rows restarted at each expert's first row (expert e owns rows
+// [offs[e-1], offs[e])), codes written transposed into q_t [cols, ld_q] with
+// run r at columns [128 r, 128 r + 128) (zero codes past a short run's last
+// row), scales [runs, cols].  ld_q >= 128 x the run count.
+hipError_t launch_quant_grouped_128x1(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                      const int32_t* offsets, int64_t E, uint8_t* q_t, int64_t ld_q, float* scale,
+                                      hipStream_t st);
+
 // Scale application of a GEMM.
 enum class Epi : int {
   Tensor = 0,       // out = acc * sa[0] * sb[0]
@@ -56,6 +65,14 @@ struct GemmProblem {
   int64_t out_row0;
   int64_t split_stride;
   int splits;
+  // Grouped weight gradient (group_k): E problems of M x N, problem e
+  // contracting over expert e's runs of 128 tokens on a token axis padded
+  // per expert to whole runs (lda = ldb = its length); offsets give the
+  // experts' token ranges, clamped to [0, tokens]; A scales [runs, M], B
+  // scales [runs, N] (1x128 x 128x1 along the tokens); problem e written at
+  // out + e M ldo.
+  bool group_k;
+  int64_t tokens;
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st);

@@ -12,6 +12,7 @@
 // on the bf16 bit patterns (|x| orders like the integer x & 0x7FFF), so the
 // reductions are integer max operations and are exact and order-free.
 #include "fp8_codec.hpp"
+#include "grouped.hpp"
 #include "launch.hpp"
 
 namespace fp8mm {
@@ -267,22 +268,42 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(
 // 128 columns, row scales scale_row[kb * rows + row] (kb = the tile's column
 // block), row codes q_row[row, col].  One read of x gives both operands of a
 // linear layer's backward that come from grad_output.
-template <bool TRANSPOSE, bool DUAL>
+//
+// GROUPED (with TRANSPOSE): the grouped weight gradient's runs.  Workgroup x
+// takes run blockIdx.x counted over all experts (expert e owns rows
+// [offs[e-1], offs[e])): the run's rows (fewer than 128 at an expert's end,
+// the missing rows read as zeros, i.e. zero codes), its codes at columns
+// [128 run, 128 run + 128) of q and its scales at row `run`; column tile
+// blockIdx.y.  Workgroups past the last run exit.
+template <bool TRANSPOSE, bool DUAL, bool GROUPED>
 __global__ __launch_bounds__(256) void quant_128x1_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale,
-    uint8_t* __restrict__ q_row, int64_t ld_q_row, float* __restrict__ scale_row) {
+    uint8_t* __restrict__ q_row, int64_t ld_q_row, float* __restrict__ scale_row,
+    const int32_t* __restrict__ offsets, int64_t E) {
+  static_assert(!GROUPED || (TRANSPOSE && !DUAL), "grouped runs: transposed codes only");
   __shared__ U16x8 colmax[4][16];
   __shared__ float col_s[128];
   __shared__ float col_r[128];
   const int t = threadIdx.x;
   const int cc = t & 15;
   const int rg = t >> 4;
-  const int64_t rb = blockIdx.y;
-  const int64_t cbase = int64_t(blockIdx.x) * 128;
+  int64_t rb = blockIdx.y;                 // scale row and output block
+  int64_t cbase = int64_t(blockIdx.x) * 128;
+  int64_t row_first = rb * 128;            // first row of x in the group
+  int rows_here = 128;                     // rows of x in the group
+  if constexpr (GROUPED) {
+    rb = blockIdx.x;
+    cbase = int64_t(blockIdx.y) * 128;
+    int e = 0;
+    int64_t row_end = 0;
+    if (!grp::find_run(offsets, E, rows, 128, int(blockIdx.x), e, row_first, row_end)) return;
+    rows_here = int(min<int64_t>(128, row_end - row_first));
+  }
   const int64_t c0 = cbase + cc * 8;
   const bool active = c0 < cols;          // cols % 8 == 0: all or nothing
-  const int64_t r0 = rb * 128 + rg * 8;
+  const int64_t r0 = rb * 128 + rg * 8;   // output row (TRANSPOSE: output column) of the thread's first row
+  const int64_t xr0 = row_first + rg * 8; // its row of x
   U16x8 v[8];
   U16x8 m;
 #pragma unroll
@@ -290,7 +311,12 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(
   if (active) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      v[i] = load16(x + (r0 + i) * ld_x + c0);
+      if (!GROUPED || rg * 8 + i < rows_here) {
+        v[i] = load16(x + (xr0 + i) * ld_x + c0);
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) v[i].w[w] = 0u;
+      }
       absmax_accum(m, v[i]);
     }
   }
@@ -499,11 +525,11 @@ hipError_t launch_quant_blockwise(const uint16_t* x, int64_t rows, int64_t cols,
   } else {
     const dim3 grid(unsigned((cols + 127) / 128), unsigned(rows / 128));
     if (transpose_out)
-      hipLaunchKernelGGL((quant_128x1_kernel<true, false>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q, ld_q,
-                         scale, nullptr, int64_t(0), nullptr);
+      hipLaunchKernelGGL((quant_128x1_kernel<true, false, false>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q,
+                         ld_q, scale, nullptr, int64_t(0), nullptr, nullptr, int64_t(0));
     else
-      hipLaunchKernelGGL((quant_128x1_kernel<false, false>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q, ld_q,
-                         scale, nullptr, int64_t(0), nullptr);
+      hipLaunchKernelGGL((quant_128x1_kernel<false, false, false>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q,
+                         ld_q, scale, nullptr, int64_t(0), nullptr, nullptr, int64_t(0));
   }
   return hipGetLastError();
 }
@@ -556,8 +582,20 @@ hipError_t launch_quant_blockwise_dual(const uint16_t* x, int64_t rows, int64_t 
                                        int64_t ld_q_col, float* scale_col, hipStream_t st) {
   if (rows == 0 || cols == 0) return hipSuccess;
   const dim3 grid(unsigned(cols / 128), unsigned(rows / 128));
-  hipLaunchKernelGGL((quant_128x1_kernel<true, true>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q_col_t, ld_q_col,
-                     scale_col, q_row, ld_q_row, scale_row);
+  hipLaunchKernelGGL((quant_128x1_kernel<true, true, false>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q_col_t,
+                     ld_q_col, scale_col, q_row, ld_q_row, scale_row, nullptr, int64_t(0));
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_grouped_128x1(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                      const int32_t* offsets, int64_t E, uint8_t* q_t, int64_t ld_q, float* scale,
+                                      hipStream_t st) {
+  if (rows == 0 || cols == 0 || E == 0) return hipSuccess;
+  // an upper bound on the run count: each expert adds at most one short run
+  const int64_t runs_max = rows / 128 + E;
+  const dim3 grid(unsigned(runs_max), unsigned((cols + 127) / 128));
+  hipLaunchKernelGGL((quant_128x1_kernel<true, false, true>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q_t, ld_q,
+                     scale, nullptr, int64_t(0), nullptr, offsets, E);
   return hipGetLastError();
 }
 

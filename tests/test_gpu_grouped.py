@@ -1,0 +1,244 @@
+"""GPU parity of the grouped (MoE) variants against the CPU oracle: the
+grouped GEMM with explicit recipes (rowwise and 1x128 x 128x128, expert
+weights read [N, K] or [K, N]), the per-expert 128x1 quantizer (bit-exact)
+and the per-expert weight gradient.
+
+The GPU and the oracle quantize the same seeded bf16 inputs independently.
+GEMM bar as for the dense GEMMs: relative Frobenius error <= 1e-3 and
+elementwise |err| <= 4e-3 * max|ref| against the float64 oracle rounded once
+to the output dtype.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import precision_matmul_amd as fp8mm
+import workloads
+from oracle import gemm, quant
+from tests.gpu_util import TOL_FRO, TOL_MAX, bf16_dev, host, out_f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _assert_close(got, ref_exact, what, out_dtype="bf16"):
+    rel_f, rel_m = gemm.parity(got, ref_exact, out_dtype)
+    say(f"{what}: rel_fro={rel_f:.3e} rel_max={rel_m:.3e}")
+    assert np.all(np.isfinite(got)), what
+    assert rel_f <= TOL_FRO and rel_m <= TOL_MAX, (what, rel_f, rel_m)
+
+
+def _offs_dev(offs):
+    return torch.from_numpy(np.asarray(offs, np.int32)).cuda()
+
+
+def _quant_block(bits, block):
+    q, s = fp8mm.fp8_quantize_blockwise(bf16_dev(bits), block)
+    rq, rs = quant.quantize_blockwise(bits, *block)
+    return q, s, rq, rs
+
+
+def _grouped_blockwise_case(E, N, K, sizes, layout, seed, with_bias=False, out_dtype=torch.bfloat16):
+    g = workloads.streams(seed, 3)
+    M = int(np.sum(sizes))
+    act = workloads.normal_bf16(g[0], (M + 5, K))                 # 5 trailing rows no expert owns
+    shape = (E, N, K) if layout == "NK" else (E, K, N)
+    W = workloads.normal_bf16(g[1], shape, 0.02)
+    bias = workloads.normal_bf16(g[2], (E, N), 0.5) if with_bias else None
+    offs = np.cumsum(sizes).astype(np.int32)
+    qa, sa, ra, rsa = _quant_block(act, (1, 128))
+    qw, sw, rw, rsw = _quant_block(W.reshape(E * shape[1], shape[2]), (128, 128))
+    grid = sw.shape[0] // E, sw.shape[1]
+    say(f"grouped blockwise E={E} N={N} K={K} {layout} bias={with_bias} {out_dtype}")
+    out = fp8mm.fp8_scaled_grouped_mm_v2(qa, qw.reshape(shape), _offs_dev(offs), sa, "1x128",
+                                         sw.reshape((E,) + grid), "128x128", b_layout=layout,
+                                         bias=None if bias is None else bf16_dev(bias), out_dtype=out_dtype)
+    ref, written = gemm.grouped_mm(ra, rw.reshape(shape), offs, rsa, rsw.reshape((E,) + grid),
+                                   bias=None if bias is None else quant.bf16_to_f32(bias), out_dtype=None,
+                                   recipe_a="1x128", recipe_b="128x128", layout=layout)
+    got = out_f64(out)
+    assert np.all(got[~written] == 0), "rows no expert owns must not be written"
+    return got[written], ref[written]
+
+
+@pytest.mark.parametrize("layout", ["NK", "KN"])
+@pytest.mark.parametrize("E,N,K,sizes", [
+    (8, 256, 512, [100, 0, 300, 1, 129, 0, 0, 256]),
+    (3, 128, 256, [5, 260, 64]),                 # N = 128: B stored [K, N] takes 128 x 128 tiles
+    (1, 384, 384, [333]),
+    (16, 384, 1024, [300, 257, 256, 255, 1, 0, 512, 40, 290, 310, 222, 260, 275, 233, 249, 301])])
+def test_grouped_blockwise(E, N, K, sizes, layout):
+    got, ref = _grouped_blockwise_case(E, N, K, np.array(sizes), layout, seed=E + N + K)
+    _assert_close(got, ref, f"grouped 1x128 x 128x128 E={E} N={N} K={K} {layout}")
+
+
+@pytest.mark.parametrize("layout", ["NK", "KN"])
+def test_grouped_blockwise_bias_fp32(layout):
+    got, ref = _grouped_blockwise_case(5, 256, 256, np.array([70, 0, 200, 3, 90]), layout, seed=5,
+                                       with_bias=True, out_dtype=torch.float32)
+    _assert_close(got, ref, f"grouped blockwise bias fp32 {layout}", out_dtype="fp32")
+
+
+@pytest.mark.parametrize("N", [128, 384])
+def test_grouped_rowwise_weights_stored_kn(N):
+    """Rowwise x rowwise with expert weights read [K, N] (scale_b per output
+    column of each expert)."""
+    E, K = 4, 256
+    sizes = np.array([40, 0, 150, 66])
+    g = workloads.streams(N + 11, 2)
+    act = workloads.normal_bf16(g[0], (int(sizes.sum()), K))
+    W = workloads.normal_bf16(g[1], (E, N, K), 0.02)              # logical [N, K] per expert
+    offs = np.cumsum(sizes).astype(np.int32)
+    qa, sa = fp8mm.fp8_quantize_rowwise(bf16_dev(act))
+    ra, rsa = quant.quantize_rowwise(act)
+    qw, sw = fp8mm.fp8_quantize_rowwise(bf16_dev(W.reshape(E * N, K)))
+    rw, rsw = quant.quantize_rowwise(W.reshape(E * N, K))
+    qw_kn = qw.reshape(E, N, K).transpose(1, 2).contiguous()      # stored [E, K, N]
+    rw_kn = np.ascontiguousarray(rw.reshape(E, N, K).transpose(0, 2, 1))
+    out = fp8mm.fp8_scaled_grouped_mm_v2(qa, qw_kn, _offs_dev(offs), sa.reshape(-1), "rowwise",
+                                         sw.reshape(-1), "rowwise", b_layout="KN")
+    ref, written = gemm.grouped_mm(ra, rw_kn, offs, rsa, rsw.reshape(E, N), out_dtype=None, layout="KN")
+    _assert_close(out_f64(out)[written], ref[written], f"grouped rowwise KN N={N}")
+
+
+def test_grouped_v2_rowwise_matches_v1():
+    E, N, K = 6, 256, 384
+    sizes = np.array([10, 200, 0, 31, 128, 77])
+    g = workloads.streams(41, 2)
+    act = workloads.normal_bf16(g[0], (int(sizes.sum()), K))
+    W = workloads.normal_bf16(g[1], (E * N, K), 0.02)
+    qa, sa = fp8mm.fp8_quantize_rowwise(bf16_dev(act))
+    qw, sw = fp8mm.fp8_quantize_rowwise(bf16_dev(W))
+    offs = _offs_dev(np.cumsum(sizes))
+    v1 = fp8mm.fp8_scaled_grouped_mm(qa, qw.reshape(E, N, K), offs, sa.reshape(-1), sw.reshape(E, N))
+    v2 = fp8mm.fp8_scaled_grouped_mm_v2(qa, qw.reshape(E, N, K), offs, sa.reshape(-1), "rowwise",
+                                        sw.reshape(-1), "rowwise")
+    assert torch.equal(v1, v2)
+
+
+def test_grouped_blockwise_full_moe_shape_sampled():
+    """E = 64, 16384 tokens, N = 1408, K = 2048 (the grouped MoE shape) in the
+    blockwise recipe, forward ([N, K] weights) and input gradient (the same
+    weights read [K, N]); 48 sampled rows (all of their columns)."""
+    inp = workloads.grouped()
+    act, W, offs = inp["act"], inp["W"], inp["offs"]
+    E, N, K = W.shape
+    M = act.shape[0]
+    qa, sa = fp8mm.fp8_quantize_blockwise(bf16_dev(act), (1, 128))
+    qw, sw = fp8mm.fp8_quantize_blockwise(bf16_dev(W.reshape(E * N, K)), (128, 128))
+    od = _offs_dev(offs)
+    say("grouped blockwise 16384x1408x2048 E=64 forward")
+    out = out_f64(fp8mm.fp8_scaled_grouped_mm_v2(qa, qw.reshape(E, N, K), od, sa, "1x128",
+                                                 sw.reshape(E, N // 128, K // 128), "128x128"))
+    rows = np.sort(np.random.default_rng(7).choice(M, 48, replace=False))
+    experts = np.searchsorted(offs, rows, side="right")
+    rq, rs = quant.quantize_blockwise(act[rows], 1, 128)            # 1x128 groups are row-local
+    got, ref = [], []
+    for t, (i, e) in enumerate(zip(rows, experts)):
+        wq, ws = quant.quantize_blockwise(W[e], 128, 128)
+        ref.append(gemm.scaled_mm_exact(rq[t:t + 1], wq, rs[:, t:t + 1], "1x128", ws, "128x128")[0])
+        got.append(out[i])
+    _assert_close(np.array(got), np.array(ref), "grouped blockwise MoE shape sampled")
+
+
+def test_grouped_blockwise_input_gradient_moe_shape_sampled():
+    """Input gradient of the grouped MoE layer: grad_output [16384, 1408]
+    (1x128) times each expert's stored [1408, 2048] weight read [K, N]."""
+    inp = workloads.grouped_backward()
+    go, W, offs = inp["grad_output"], inp["W"], inp["offs"]
+    E, Nw, Kw = W.shape                      # contraction over Nw = 1408, output width Kw = 2048
+    M = go.shape[0]
+    qg, sg = fp8mm.fp8_quantize_blockwise(bf16_dev(go), (1, 128))
+    qw, sw = fp8mm.fp8_quantize_blockwise(bf16_dev(W.reshape(E * Nw, Kw)), (128, 128))
+    say("grouped blockwise input gradient 16384x2048x1408 E=64")
+    out = out_f64(fp8mm.fp8_scaled_grouped_mm_v2(qg, qw.reshape(E, Nw, Kw), _offs_dev(offs), sg, "1x128",
+                                                 sw.reshape(E, Nw // 128, Kw // 128), "128x128", b_layout="KN"))
+    rows = np.sort(np.random.default_rng(8).choice(M, 48, replace=False))
+    experts = np.searchsorted(offs, rows, side="right")
+    rq, rs = quant.quantize_blockwise(go[rows], 1, 128)
+    got, ref = [], []
+    for t, (i, e) in enumerate(zip(rows, experts)):
+        wq, ws = quant.quantize_blockwise(W[e], 128, 128)
+        ref.append(gemm.scaled_mm_exact(rq[t:t + 1], wq, rs[:, t:t + 1], "1x128", ws, "128x128", layout="KN")[0])
+        got.append(out[i])
+    _assert_close(np.array(got), np.array(ref), "grouped blockwise input gradient sampled")
+
+
+# ------------------------------------------------------ grouped weight gradient
+
+def _check_grouped_quant(bits, offs):
+    q, s = fp8mm.fp8_quantize_grouped_128x1(bf16_dev(bits), _offs_dev(offs))
+    rq, rs, _ = quant.quantize_grouped_128x1(bits, offs)
+    nb = rs.shape[0]
+    gq, gs = host(q), host(s)
+    assert np.array_equal(gq[:, :128 * nb], rq), "grouped 128x1 codes"
+    assert np.array_equal(gs[:nb], rs), "grouped 128x1 scales"
+    return q, s, rq, rs
+
+
+@pytest.mark.parametrize("sizes,C", [
+    ([130, 5, 0, 257, 1, 128, 0, 300], 64),
+    ([0, 0, 0], 32),
+    ([1000], 48),
+    ([128] * 9, 256)])
+def test_grouped_128x1_quant_bit_exact(sizes, C):
+    offs = np.cumsum(sizes).astype(np.int32)
+    T = int(offs[-1]) + 3                                       # 3 trailing rows no expert owns
+    x = workloads.normal_bf16(workloads.streams(len(sizes) + C, 1)[0], (T, C), 2.0)
+    say(f"grouped 128x1 quant sizes={sizes} C={C}")
+    _check_grouped_quant(x, offs)
+
+
+def _grouped_grad_weight_case(sizes, N_out, K_in, seed, out_dtype):
+    offs = np.cumsum(sizes).astype(np.int32)
+    T = int(offs[-1]) + 2
+    g = workloads.streams(seed, 2)
+    go = workloads.normal_bf16(g[0], (T, N_out), 1e-3)
+    x = workloads.normal_bf16(g[1], (T, K_in))
+    qg, sg, rqg, rsg = _check_grouped_quant(go, offs)
+    qx, sx, rqx, rsx = _check_grouped_quant(x, offs)
+    say(f"grouped grad_weight sizes={list(sizes)} N_out={N_out} K_in={K_in} {out_dtype}")
+    out = fp8mm.fp8_grouped_linear_grad_weight(qg, sg, qx, sx, _offs_dev(offs), T, out_dtype=out_dtype)
+    ref = gemm.grouped_grad_weight(rqg, rsg, rqx, rsx, offs, out_dtype=None)
+    return out_f64(out), ref
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("sizes,N_out,K_in", [
+    ([130, 0, 5, 257, 128, 1], 256, 384),
+    ([40, 90], 208, 144),                      # ragged output tiles
+    ([700], 128, 128),
+    ([3] * 20, 64, 256)])
+def test_grouped_weight_gradient(sizes, N_out, K_in, out_dtype):
+    got, ref = _grouped_grad_weight_case(np.array(sizes), N_out, K_in, seed=N_out + K_in, out_dtype=out_dtype)
+    od = "bf16" if out_dtype == torch.bfloat16 else "fp32"
+    for e, m in enumerate(sizes):
+        if m == 0:
+            assert not got[e].any(), "an expert without tokens gets zeros"
+    _assert_close(got, ref, f"grouped grad_weight {sizes} {N_out}x{K_in}", out_dtype=od)
+
+
+def test_grouped_weight_gradient_moe_shape():
+    """E = 64 experts over 16384 tokens, grad_output [16384, 1408], input
+    [16384, 2048]: the quantizer on the full shape (bit-exact) and the
+    gradients of 6 experts in full."""
+    inp = workloads.grouped_backward()
+    go, x, offs = inp["grad_output"], inp["act"], inp["offs"]
+    T = go.shape[0]
+    say("grouped 128x1 quant + grad_weight, MoE shape")
+    qg, sg, rqg, rsg = _check_grouped_quant(go, offs)
+    qx, sx, rqx, rsx = _check_grouped_quant(x, offs)
+    out = out_f64(fp8mm.fp8_grouped_linear_grad_weight(qg, sg, qx, sx, _offs_dev(offs), T))
+    assert out.shape == (64, 1408, 2048)
+    pick = [0, 1, 17, 40, 62, 63]
+    sizes = np.diff(np.concatenate([[0], offs]))
+    # the oracle on the picked experts only: the same runs, the other experts emptied
+    keep = np.zeros(64, bool)
+    keep[pick] = True
+    sub = np.cumsum(np.where(keep, sizes, 0)).astype(np.int32)
+    starts = np.concatenate([[0], offs[:-1]])
+    rows = np.concatenate([np.arange(starts[e], offs[e]) for e in pick])
+    rqg2, rsg2, _ = quant.quantize_grouped_128x1(go[rows], sub)
+    rqx2, rsx2, _ = quant.quantize_grouped_128x1(x[rows], sub)
+    ref = gemm.grouped_grad_weight(rqg2, rsg2, rqx2, rsx2, sub, out_dtype=None)
+    _assert_close(out[pick], ref[pick], "grouped grad_weight MoE shape, 6 experts")

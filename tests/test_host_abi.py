@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -105,6 +105,54 @@ def test_grouped_requires_offsets_and_checks_shapes(lib):
     assert f(FAKE, 64, 256, FAKE, -1, 64, FAKE, FAKE, FAKE, None, 0, FAKE, 64, None) == _lib.EINVAL
     assert f(FAKE, 64, 256, FAKE, 4, 64, FAKE, FAKE, FAKE, None, 0, FAKE, 32, None) == _lib.EINVAL
     assert f(FAKE, 64, 256, FAKE, 4, 64, FAKE, FAKE, FAKE, None, 9, FAKE, 64, None) == _lib.EINVAL
+
+
+def test_grouped_v2_checks_recipes_and_shapes(lib):
+    f = lib.fp8_scaled_grouped_mm_v2
+
+    def call(**kw):
+        a = dict(A=FAKE, M=64, K=256, B=FAKE, E=4, N=128, layout=0, offs=FAKE, sa=FAKE, ra=2, sb=FAKE, rb=3,
+                 bias=None, od=0, out=FAKE, ldo=128)
+        a.update(kw)
+        return f(a["A"], a["M"], a["K"], a["B"], a["E"], a["N"], a["layout"], a["offs"], a["sa"], a["ra"], a["sb"],
+                 a["rb"], a["bias"], a["od"], a["out"], a["ldo"], None)
+
+    assert call(offs=None) == _lib.EINVAL
+    assert call(ra=0, rb=0) == _lib.ENOTIMPL                   # tensorwise grouped
+    assert call(ra=2, rb=4) == _lib.ENOTIMPL                   # 1x128 x 128x1 grouped
+    assert call(ra=5, rb=5) == _lib.ENOTIMPL                   # mxfp8 grouped
+    assert call(ra=7) == _lib.EINVAL                           # unknown enum
+    assert call(K=192) == _lib.EINVAL                          # blockwise K % 128
+    assert call(N=64, ldo=64) == _lib.EINVAL                   # 128x128 needs N % 128
+    assert call(layout=2) == _lib.EINVAL
+    assert call(ra=1, rb=1, layout=1, N=24, ldo=24) == _lib.EINVAL   # B stored [K, N]: N % 16
+    assert call(ldo=64) == _lib.EINVAL
+    assert call(A=FAKE + 8) == _lib.EINVAL
+    assert call(E=-1) == _lib.EINVAL
+    assert call(M=0) == _lib.OK                                # empty: nothing to do
+
+
+def test_grouped_weight_gradient_entries_check_capacity(lib):
+    assert lib.fp8mm_grouped_runs_capacity(16384, 64) == 128 + 64
+    assert lib.fp8mm_grouped_runs_capacity(127, 3) == 3
+    assert lib.fp8mm_grouped_runs_capacity(-1, 3) == -1
+    q = lib.fp8_quantize_grouped_128x1
+    # x, T, C, ld_x, offsets, E, q_t, ld_q, scale, stream
+    cap = 128 * (1000 // 128 + 8)
+    assert q(FAKE, 1000, 64, 64, FAKE, 8, FAKE, cap - 16, FAKE, None) == _lib.EINVAL    # ld_q below the runs
+    assert q(FAKE, 1000, 64, 64, None, 8, FAKE, cap, FAKE, None) == _lib.EINVAL         # offsets NULL
+    assert q(FAKE, 1000, 72, 72, FAKE, 8, FAKE, cap, FAKE, None) == _lib.EINVAL         # C % 16
+    assert q(FAKE, 1000, 64, 64, FAKE, 8, FAKE, cap + 8, FAKE, None) == _lib.EINVAL     # ld_q % 16
+    assert q(FAKE, 1000, 64, 64, FAKE, 8, FAKE, cap, None, None) == _lib.EINVAL         # scale NULL
+    assert q(FAKE, 1000, 64, 64, FAKE, -1, FAKE, cap, FAKE, None) == _lib.EINVAL
+    g = lib.fp8_grouped_linear_grad_weight
+    # gt_q, N_out, gt_scale, xt_q, K_in, xt_scale, ld, T, offsets, E, od, grad_w, stream
+    assert g(FAKE, 64, FAKE, FAKE, 64, FAKE, cap - 128, 1000, FAKE, 8, 0, FAKE, None) == _lib.EINVAL
+    assert g(FAKE, 64, FAKE, FAKE, 64, FAKE, cap, 1000, None, 8, 0, FAKE, None) == _lib.EINVAL
+    assert g(FAKE, 64, FAKE, FAKE, 64, FAKE, cap, 1000, FAKE, 8, 4, FAKE, None) == _lib.EINVAL
+    assert g(FAKE + 4, 64, FAKE, FAKE, 64, FAKE, cap, 1000, FAKE, 8, 0, FAKE, None) == _lib.EINVAL
+    assert g(FAKE, 64, None, FAKE, 64, FAKE, cap, 1000, FAKE, 8, 0, FAKE, None) == _lib.EINVAL
+    assert g(FAKE, 0, FAKE, FAKE, 64, FAKE, cap, 1000, FAKE, 8, 0, FAKE, None) == _lib.OK
 
 
 def test_quantizers_reject_before_launch(lib):
