@@ -164,6 +164,7 @@ def build_workloads(torch, fp8mm, workloads):
         Wd = _dev_bf16(inp["W"].reshape(E * N, K), torch)
         offs = torch.from_numpy(inp["offs"]).cuda()
         M = int(inp["offs"][-1])
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         state = {}
 
         def quant():
@@ -172,12 +173,65 @@ def build_workloads(torch, fp8mm, workloads):
 
         def gemm():
             return fp8mm.fp8_scaled_grouped_mm(state["qa"], state["qw"].view(E, N, K), offs, state["sa"],
-                                               state["sw"].view(E, N))
+                                               state["sw"].view(E, N), out=out)
 
         return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
                     gemm_bytes=M * K + E * N * K + 4 * (M + E * N) + 4 * E + 2 * M * N,
                     quant_bytes=3 * (M * K + E * N * K) + 4 * (M + E * N), shape=(M, N, K, E),
                     recipe="grouped_rowwise_E64")
+
+    def grouped_blockwise(layout):
+        # NK: the MoE forward, out [16384, 1408] = act [16384, 2048] @ W[e]^T;
+        # KN: its input gradient, [16384, 2048] = grad_output [16384, 1408] @
+        # W[e], the stored [1408, 2048] expert weights read [K, N]
+        inp = workloads.grouped_backward()
+        E, Nw, Kw = inp["W"].shape
+        Wd = _dev_bf16(inp["W"].reshape(E * Nw, Kw), torch)
+        a = _dev_bf16(inp["act"] if layout == "NK" else inp["grad_output"], torch)
+        offs = torch.from_numpy(inp["offs"]).cuda()
+        M = int(inp["offs"][-1])
+        N, K = (Nw, Kw) if layout == "NK" else (Kw, Nw)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        state = {}
+
+        def quant():
+            state["qa"], state["sa"] = fp8mm.fp8_quantize_blockwise(a, (1, 128))
+            state["qw"], state["sw"] = fp8mm.fp8_quantize_blockwise(Wd, (128, 128))
+
+        def gemm():
+            return fp8mm.fp8_scaled_grouped_mm_v2(state["qa"], state["qw"].view(E, Nw, Kw), offs, state["sa"], "1x128",
+                                                  state["sw"].view(E, Nw // 128, Kw // 128), "128x128",
+                                                  b_layout=layout, out=out)
+
+        scales = 4 * ((K // 128) * M + E * (Nw // 128) * (Kw // 128))
+        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+                    gemm_bytes=M * K + E * N * K + scales + 4 * E + 2 * M * N,
+                    quant_bytes=3 * (M * K + E * N * K) + scales, shape=(M, N, K, E),
+                    recipe="grouped_blockwise_1x128_128x128" + (" (KN)" if layout == "KN" else ""))
+
+    def grouped_grad_weight():
+        # grad_w[e] [1408, 2048] = grad_output[rows_e].t() @ act[rows_e], 64 experts
+        inp = workloads.grouped_backward()
+        g, x = _dev_bf16(inp["grad_output"], torch), _dev_bf16(inp["act"], torch)
+        offs = torch.from_numpy(inp["offs"]).cuda()
+        T, N_out = g.shape
+        K_in = x.shape[1]
+        E = offs.numel()
+        runs = int(np.sum((np.diff(np.concatenate([[0], inp["offs"]])) + 127) // 128))
+        state = {}
+
+        def quant():
+            state["qg"], state["sg"] = fp8mm.fp8_quantize_grouped_128x1(g, offs)
+            state["qx"], state["sx"] = fp8mm.fp8_quantize_grouped_128x1(x, offs)
+
+        def gemm():
+            return fp8mm.fp8_grouped_linear_grad_weight(state["qg"], state["sg"], state["qx"], state["sx"], offs, T)
+
+        scales = 4 * runs * (N_out + K_in)
+        return dict(quant=quant, gemm=gemm, flops=2.0 * T * N_out * K_in,
+                    gemm_bytes=T * (N_out + K_in) + scales + 4 * E + 2 * E * N_out * K_in,
+                    quant_bytes=3 * T * (N_out + K_in) + scales, shape=(N_out, K_in, T, E),
+                    recipe="grouped_weight_gradient_1x128_128x1")
 
     W["tensorwise_256"] = lambda: tensorwise(256)
     W["rowwise_8192x4096x4096"] = lambda: rowwise(8192, 4096, 4096)
@@ -188,6 +242,9 @@ def build_workloads(torch, fp8mm, workloads):
     W["blockwise_grad_weight_5120x8192x16640"] = lambda: blockwise_grad_weight(16640, 5120, 8192)
     W["grouped_moe_E64_16384x1408x2048"] = grouped
     W["mxfp8_16640x5120x8192"] = lambda: mxfp8(16640, 5120, 8192)
+    W["grouped_blockwise_E64_16384x1408x2048"] = lambda: grouped_blockwise("NK")
+    W["grouped_blockwise_grad_input_E64_16384x2048x1408"] = lambda: grouped_blockwise("KN")
+    W["grouped_grad_weight_E64_1408x2048_T16384"] = grouped_grad_weight
     return W
 
 
