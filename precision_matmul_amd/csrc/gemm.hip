@@ -754,6 +754,7 @@ hipError_t launch_tail_splitk(const GemmProblem& p, int splits, float* scratch, 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
   if (p.group_k) {
     if (p.epi != Epi::Block128x1 || p.b_kn || p.bias || !p.offsets) return hipErrorInvalidValue;
+    if (p.lda >= 128 && p.ldb >= 128) return launch_gemm_group_k_streaming(p, st);
     return p.out_bf16 ? launch_group_k<true>(p, st) : launch_group_k<false>(p, st);
   }
   if (p.offsets) {

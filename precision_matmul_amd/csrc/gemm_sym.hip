@@ -72,7 +72,9 @@ __device__ __forceinline__ float fac(const v4f& f, int e) { return f[e]; }
 __device__ __forceinline__ int kswz(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
 __device__ __forceinline__ int kn_off(int k, int n) { return k * 256 + (((n >> 4) ^ kswz(k)) << 4) + (n & 15); }
 
-template <Epi EPI, bool OUT_BF16, bool BIAS, bool K_ALIGNED, bool B_KN, bool GROUPED>
+// GROUPED_K: the grouped weight gradient, E problems of M x N that contract
+// over the experts' runs of 128 tokens (offsets along K).
+template <Epi EPI, bool OUT_BF16, bool BIAS, bool K_ALIGNED, bool B_KN, bool GROUPED, bool GROUPED_K = false>
 __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                                    int vec_out) {
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
@@ -88,6 +90,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   constexpr bool MX = EPI == Epi::MX;
   static_assert(!MX || (!B_KN && !GROUPED), "MXFP8: plain GEMMs with B stored [N, K]");
   static_assert(!GROUPED || EPI == Epi::Row || EPI == Epi::Block128x128, "grouped: rowwise or 1x128 x 128x128");
+  static_assert(!GROUPED_K || (EPI == Epi::Block128x1 && !B_KN && !GROUPED && !BIAS), "grouped weight gradient");
   using Fac = std::conditional_t<SWAP, float, v4f>;
   constexpr int OUTB = OUT_BF16 ? 2 : 4;
   constexpr int EPI_PASSES = epi_passes(SY_NW, SY_TM, SY_TN, OUTB, SY_STAGE);
@@ -115,10 +118,43 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   int tn;
   int64_t row0;
   int rows_valid;
+  const uint8_t* Ag = p.A;
   const uint8_t* Bg = p.B;
+  const float* sag = p.sa;
   const float* sbg = p.sb;
   [[maybe_unused]] const uint16_t* biasg = p.bias;
-  if constexpr (GROUPED) {
+  int K = int(p.K);
+  int64_t out_off = 0;
+  if constexpr (GROUPED_K) {
+    // Expert e = lin / (tiles_m tiles_n): one expert's tiles are consecutive
+    // in one XCD, whose L2 then holds that expert's operand columns: columns
+    // [128 first, 128 (first + runs)) of the padded token axis, scale rows
+    // [first, first + runs) of [runs, M] and [runs, N]; output problem e of
+    // [E, M, N].
+    const int64_t per_xcd = gridDim.x / 8;   // the launcher pads the grid to a multiple of 8
+    const int64_t lin = int64_t(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    const int64_t tiles = int64_t(tiles_m) * tiles_n;
+    const int64_t e = lin / tiles;
+    if (e >= p.E) return;
+    const int t = int(lin - e * tiles);
+    tn = t % tiles_n;
+    int64_t first = 0;
+    int runs = 0;
+    grp::runs_before(p.offsets, p.tokens, 128, e, first, runs);
+    // the operands and scales hold lda / 128 runs; offsets that are not
+    // non-decreasing could ask for more, which are dropped
+    const int64_t cap = p.lda / 128;
+    first = min(first, cap);
+    runs = int(min<int64_t>(runs, cap - first));
+    row0 = int64_t(t / tiles_n) * SY_BM;
+    rows_valid = int(min<int64_t>(SY_BM, p.M - row0));
+    Ag = p.A + first * 128;
+    Bg = p.B + first * 128;
+    sag = p.sa + first * p.M;
+    sbg = p.sb + first * p.N;
+    K = runs * 128;
+    out_off = e * p.M * p.ldo;
+  } else if constexpr (GROUPED) {
     const int r = blockIdx.x / 8;
     const int g = (r / tiles_n) * 8 + blockIdx.x % 8;
     tn = r % tiles_n;
@@ -138,7 +174,6 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   }
   const int64_t n0 = int64_t(tn) * SY_BN;
   const int cols_valid = int(min<int64_t>(SY_BN, p.N - n0));
-  const int K = int(p.K);
   const int nk = (K + BK - 1) / BK;
 
   // ---------------- loaders ----------------
@@ -151,7 +186,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   const int ld_row = lane >> 3;
   const int ch_even = (lane & 7) ^ (lane >> 4);
   const int ch_odd = (lane & 7) ^ (4 | (lane >> 4));
-  const Rsrc rsA = make_rsrc4(p.A + row0 * p.lda, uint32_t(rows_valid) * uint32_t(p.lda));
+  const Rsrc rsA = make_rsrc4(Ag + row0 * p.lda, uint32_t(rows_valid) * uint32_t(p.lda));
   [[maybe_unused]] const Rsrc rsB = make_rsrc4(Bg + n0 * p.ldb, uint32_t(cols_valid) * uint32_t(p.ldb));
   const uint32_t rowA = uint32_t(wave * 32 + ld_row) * uint32_t(p.lda);
   const uint32_t rowB = uint32_t(wave * 32 + ld_row) * uint32_t(p.ldb);
@@ -216,7 +251,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   [[maybe_unused]] int64_t sc_stride = 0;    // elements per K step
   if constexpr (BLOCKWISE) {
     if (wave < 4) {
-      sc_base = p.sa + row0 + wave * 64;
+      sc_base = sag + row0 + wave * 64;
       sc_count = int64_t(nk) * p.M - row0 - wave * 64;
       sc_stride = p.M;
     } else if constexpr (EPI == Epi::Block128x1) {
@@ -251,7 +286,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       const int64_t first = (wave < 4 ? row0 : n0) + 64 * w4;
       const int valid = wave < 4 ? rows_valid : cols_valid;
       const int here = min(max(valid - 64 * w4, 0), 64);
-      const uint8_t* base = (wave < 4 ? reinterpret_cast<const uint8_t*>(p.sa) : reinterpret_cast<const uint8_t*>(sbg)) +
+      const uint8_t* base = (wave < 4 ? reinterpret_cast<const uint8_t*>(sag) : reinterpret_cast<const uint8_t*>(sbg)) +
                             (here > 0 ? first * nkb : 0);
       const Rsrc r = make_rsrc4(base, uint32_t(here) * uint32_t(nkb));
       dma_b32(r, st + SY_A + SY_B + (wave < 4 ? 0 : SY_SCALE) + w4 * 256,
@@ -614,7 +649,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       const int ct = col_base + pass * EPI_COLS + ch * EPR;
       if (rt >= rows_valid || ct >= cols_valid) continue;
       const uint8_t* src = ep + rl * EPI_PITCH + ch * 16;
-      uint8_t* dst = reinterpret_cast<uint8_t*>(p.out) + ((row0 + rt) * p.ldo + n0 + ct) * OUTB;
+      uint8_t* dst = reinterpret_cast<uint8_t*>(p.out) + (out_off + (row0 + rt) * p.ldo + n0 + ct) * OUTB;
       if (vec_out && ct + EPR <= cols_valid) {
         *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
       } else {
@@ -683,7 +718,27 @@ hipError_t launch_sym_out(const GemmProblem& p, hipStream_t st) {
   return bias ? launch_sym<EPI, false, true, false, false>(p, st) : launch_sym<EPI, false, false, false, false>(p, st);
 }
 
+// The grouped weight gradient on 256 x 256 tiles: grid E x tiles, padded to
+// a multiple of 8.
+template <bool OUT_BF16>
+hipError_t launch_sym_group_k(const GemmProblem& p, hipStream_t st) {
+  const int tiles_m = int((p.M + SY_BM - 1) / SY_BM), tiles_n = int((p.N + SY_BN - 1) / SY_BN);
+  const int64_t total = int64_t(tiles_m) * tiles_n * p.E;
+  if (total == 0) return hipSuccess;
+  const int64_t grid = (total + 7) / 8 * 8;
+  if (grid > int64_t(INT32_MAX)) return hipErrorInvalidValue;
+  const int outb = OUT_BF16 ? 2 : 4;
+  const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
+  hipLaunchKernelGGL((gemm_sym_kernel<Epi::Block128x1, OUT_BF16, false, true, false, false, true>),
+                     dim3(unsigned(grid)), dim3(SY_NW * 64), 0, st, p, tiles_m, tiles_n, vec_out);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_gemm_group_k_streaming(const GemmProblem& p, hipStream_t st) {
+  return p.out_bf16 ? launch_sym_group_k<true>(p, st) : launch_sym_group_k<false>(p, st);
+}
 
 // Streaming schedule: plain GEMMs (B stored [N, K] or [K, N]) and grouped
 // rowwise or 1x128 x 128x128 GEMMs (expert weights [E, N, K] or [E, K, N]).

@@ -78,5 +78,7 @@ struct GemmProblem {
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st);
 // Streaming schedule, 256 x 256 tiles: plain GEMMs and grouped rowwise GEMMs.
 hipError_t launch_gemm_streaming(const GemmProblem& p, hipStream_t st);
+// The grouped weight gradient (group_k) on the streaming kernel's 256 x 256 tiles.
+hipError_t launch_gemm_group_k_streaming(const GemmProblem& p, hipStream_t st);
 
 }  // namespace fp8mm
