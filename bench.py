@@ -490,6 +490,35 @@ def main():
                     "grad_output, grad_input GEMM, grad_weight GEMM"}
         del xl, wl_, gl
         torch.cuda.empty_cache()
+        # The MoE expert layer as one autograd op (E = 64, 16384 tokens,
+        # K_in = 2048, N_out = 1408): grouped forward, grouped input gradient
+        # and per-expert weight gradient with every quantize.
+        print("[bench] grouped (MoE) layer step (forward + backward)", file=sys.stderr, flush=True)
+        inp = workloads.grouped_backward()
+        xg = _dev_bf16(inp["act"], torch).requires_grad_(True)
+        E_, N_, K_ = inp["W"].shape
+        wg = _dev_bf16(inp["W"], torch).requires_grad_(True)
+        gg = _dev_bf16(inp["grad_output"], torch)
+        og = torch.from_numpy(inp["offs"]).cuda()
+        Tg = int(inp["offs"][-1])
+        del inp
+
+        def moe_step():
+            xg.grad = None
+            wg.grad = None
+            fp8mm.fp8_grouped_linear(xg, wg, og).backward(gg)
+
+        m_med, _, m_min, m_max = time_kernel(torch, moe_step, 10, warmup=3)
+        m_flops = 3 * 2.0 * Tg * N_ * K_
+        result["grouped_layer_step"] = {
+            "shape_T_Kin_Nout_E": [Tg, K_, N_, E_], "ms": round(m_med, 4),
+            "ms_min_max": [round(m_min, 4), round(m_max, 4)],
+            "tflops": round(m_flops / (m_med * 1e-3) / 1e12, 2),
+            "step": "1x128 and per-expert 128x1 quantize of x, 128x128 quantize of the expert weights, grouped "
+                    "forward; 1x128 and per-expert 128x1 quantize of grad_output, grouped input gradient, "
+                    "per-expert weight gradient"}
+        del xg, wg, gg, og
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -22,7 +22,7 @@ __all__ = [
     "fp8_scaled_mm", "fp8_scaled_grouped_mm", "fp8_scaled_grouped_mm_v2", "grouped_runs_capacity",
     "fp8_quantize_grouped_128x1", "fp8_grouped_linear_grad_weight", "fp8_linear_forward",
     "fp8_linear_grad_input", "fp8_linear_grad_weight", "recipe_pair_supported",
-    "FP8BlockwiseLinear", "fp8_blockwise_linear",
+    "FP8BlockwiseLinear", "fp8_blockwise_linear", "FP8GroupedLinear", "fp8_grouped_linear",
 ]
 
 ROWWISE_EPS = 1e-12
@@ -411,4 +411,5 @@ def recipe_pair_supported(recipe_a, recipe_b, b_layout="NK"):
                                                         _lib.B_LAYOUTS[b_layout]))
 
 
-from .linear import FP8BlockwiseLinear, fp8_blockwise_linear  # noqa: E402  (uses the functions above)
+from .linear import (FP8BlockwiseLinear, FP8GroupedLinear, fp8_blockwise_linear,  # noqa: E402  (uses the functions above)
+                     fp8_grouped_linear)

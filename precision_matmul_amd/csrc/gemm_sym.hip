@@ -651,7 +651,9 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       const uint8_t* src = ep + rl * EPI_PITCH + ch * 16;
       uint8_t* dst = reinterpret_cast<uint8_t*>(p.out) + (out_off + (row0 + rt) * p.ldo + n0 + ct) * OUTB;
       if (vec_out && ct + EPR <= cols_valid) {
-        if constexpr (GROUPED_K)
+        // Grouped outputs: non-temporal stores, measured 3-15 % faster there
+        // (no gain measured on the dense GEMMs, which keep plain stores)
+        if constexpr (GROUPED || GROUPED_K)
           __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(src), reinterpret_cast<v4i*>(dst));
         else
           *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);

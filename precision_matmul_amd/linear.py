@@ -22,8 +22,9 @@ FP8 path.
 
 import torch
 
-from . import (fp8_linear_forward, fp8_linear_grad_input, fp8_linear_grad_weight, fp8_quantize_blockwise,
-               fp8_quantize_blockwise_dual)
+from . import (fp8_grouped_linear_grad_weight, fp8_linear_forward, fp8_linear_grad_input, fp8_linear_grad_weight,
+               fp8_quantize_blockwise, fp8_quantize_blockwise_dual, fp8_quantize_grouped_128x1,
+               fp8_scaled_grouped_mm_v2)
 
 
 class FP8BlockwiseLinear(torch.autograd.Function):
@@ -57,3 +58,54 @@ class FP8BlockwiseLinear(torch.autograd.Function):
 def fp8_blockwise_linear(x, w):
     """x @ w.t() through FP8BlockwiseLinear (differentiable in x and w)."""
     return FP8BlockwiseLinear.apply(x, w)
+
+
+class FP8GroupedLinear(torch.autograd.Function):
+    """MoE expert layer y[rows_e] = x[rows_e] @ w[e].t() for every expert e,
+    expert e owning token rows [offs[e-1], offs[e]) (the grouped form of
+    pytorch/ao PR #4390), in the blockwise recipe applied per expert:
+
+      forward:  x -> 1x128 codes (forward GEMM) and per-expert 128-token runs
+                     written transposed (kept for grad_weight)
+                w [E, N_out, K_in] -> 128x128 codes per expert (kept)
+                y = grouped GEMM, expert weights read [N, K]
+      backward: grad_out -> 1x128 codes and per-expert runs
+                grad_x    = grouped GEMM, the same weight codes read [K, N]
+                grad_w[e] = grad_out[rows_e].t() @ x[rows_e]
+
+    x [T, K_in], w [E, N_out, K_in] bf16, offs int32 [E] on the GPU; K_in and
+    N_out multiples of 128.  Rows of y and grad_x at or past offs[E-1] are 0."""
+
+    @staticmethod
+    def forward(ctx, x, w, offs):
+        if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+            raise ValueError("x and w must be bf16")
+        x = x.contiguous()
+        w = w.contiguous()
+        E, N_out, K_in = w.shape
+        qx, sx = fp8_quantize_blockwise(x, (1, 128))
+        qxt, sxt = fp8_quantize_grouped_128x1(x, offs)
+        qw, sw = fp8_quantize_blockwise(w.view(E * N_out, K_in), (128, 128))
+        qw = qw.view(E, N_out, K_in)
+        sw = sw.view(E, N_out // 128, K_in // 128)
+        ctx.save_for_backward(qxt, sxt, qw, sw, offs)
+        ctx.tokens = x.shape[0]
+        return fp8_scaled_grouped_mm_v2(qx, qw, offs, sx, "1x128", sw, "128x128")
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        qxt, sxt, qw, sw, offs = ctx.saved_tensors
+        g = grad_out.to(torch.bfloat16).contiguous()
+        grad_x = grad_w = None
+        if ctx.needs_input_grad[0]:
+            qg, sg = fp8_quantize_blockwise(g, (1, 128))
+            grad_x = fp8_scaled_grouped_mm_v2(qg, qw, offs, sg, "1x128", sw, "128x128", b_layout="KN")
+        if ctx.needs_input_grad[1]:
+            qgt, sgt = fp8_quantize_grouped_128x1(g, offs)
+            grad_w = fp8_grouped_linear_grad_weight(qgt, sgt, qxt, sxt, offs, ctx.tokens)
+        return grad_x, grad_w, None
+
+
+def fp8_grouped_linear(x, w, offs):
+    """The MoE expert layer through FP8GroupedLinear (differentiable in x and w)."""
+    return FP8GroupedLinear.apply(x, w, offs)
