@@ -305,7 +305,7 @@ def cpu_baseline(workloads):
                       f"({2.0 * Ms * N * K / 1e9:.0f} GFLOP), rounding to bf16"}
 
 
-GEMM_SOURCES = ("gemm.hip", "gemm_sym.hip", "gemm_common.hpp", "launch.hpp")
+GEMM_SOURCES = ("gemm.hip", "gemm_sym.hip", "gemm_common.hpp", "grouped.hpp", "launch.hpp")
 
 
 def gemm_source_sha():
