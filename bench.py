@@ -276,6 +276,39 @@ def time_kernel(torch, fn, iters, warmup=3):
     return t[len(t) // 2], float(np.mean(t)), t[0], t[-1]
 
 
+def time_graph(torch, fn, calls=10, iters=20):
+    """Device time (ms) per call of fn replayed from a HIP graph that holds
+    `calls` back-to-back calls (no host launch gaps): median over iters
+    replays / calls.  None if the calls cannot be captured."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(iters):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            g.replay()
+            e.record()
+            evs.append((s, e))
+        torch.cuda.synchronize()
+        t = sorted(s.elapsed_time(e) for s, e in evs)
+        del g
+        return t[len(t) // 2] / calls
+    except RuntimeError as exc:
+        print(f"[bench] graph capture failed: {exc}", file=sys.stderr, flush=True)
+        return None
+
+
 def cpu_baseline(workloads):
     """The oracle (untuned numpy + OpenBLAS float64) on a bounded sample of the
     default workload: rows [0, 12480) of the 16640x5120x8192 blockwise forward
@@ -429,8 +462,10 @@ def main():
             q_med, _, q_min, q_max = time_kernel(torch, w2["quant"], 20)
             g_med, _, g_min, g_max = time_kernel(torch, w2["gemm"], 50, warmup=10)
             q_gbs = w2["quant_bytes"] / (q_med * 1e-3) / 1e9
+            g_graph = time_graph(torch, w2["gemm"])
             per[name] = {"recipe": w2["recipe"], "gemm_ms": round(g_med, 4),
                          "gemm_ms_min_max": [round(g_min, 4), round(g_max, 4)],
+                         "gemm_ms_graph": None if g_graph is None else round(g_graph, 4),
                          "gemm_tflops": round(w2["flops"] / (g_med * 1e-3) / 1e12, 2),
                          "gemm_frac_fp8_peak": round(w2["flops"] / (g_med * 1e-3) / 1e12 / FP8_DENSE_PEAK_TFLOPS, 4),
                          "quant_ms": round(q_med, 4),
