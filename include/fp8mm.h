@@ -179,7 +179,9 @@ fp8mm_status fp8_quantize_blockwise_dual(const void* x, int64_t rows,
  *   (BLOCK_1x128, BLOCK_128x128)  (BLOCK_1x128, BLOCK_128x1)
  *   (MXFP8, MXFP8) with B_NK (B_KN -> FP8MM_ENOTIMPL)
  * K % 16 == 0; blockwise and MXFP8 recipes need K % 128 == 0 and, for
- * BLOCK_128x128, N % 128 == 0.  M, N or K of 0 is allowed. */
+ * BLOCK_128x128, N % 128 == 0; blockwise scale arrays of more than 2^30
+ * elements ((K/128) M or (K/128) N) are FP8MM_EINVAL.  M, N or K of 0 is
+ * allowed. */
 fp8mm_status fp8_scaled_mm(const uint8_t* A, int64_t M, int64_t K, int64_t lda,
                            const uint8_t* B, int64_t N, int64_t ldb,
                            fp8mm_b_layout b_layout, const float* scale_a,

@@ -80,6 +80,7 @@ def _mm(lib, **kw):
     (dict(ra=5, rb=5, K=160, lda=160, ldb=160), _lib.EINVAL),      # mxfp8 K % 128
     (dict(ra=5, rb=2), _lib.ENOTIMPL),                             # mxfp8 x 1x128
     (dict(ra=6), _lib.EINVAL),                                     # unknown enum
+    (dict(ra=2, rb=3, M=2 ** 30), _lib.EINVAL),                    # 1x128 scales above 2^30 elements
 ])
 def test_scaled_mm_rejects_before_launch(lib, kw, code):
     assert _mm(lib, **kw) == code
@@ -153,6 +154,8 @@ def test_grouped_weight_gradient_entries_check_capacity(lib):
     assert g(FAKE + 4, 64, FAKE, FAKE, 64, FAKE, cap, 1000, FAKE, 8, 0, FAKE, None) == _lib.EINVAL
     assert g(FAKE, 64, None, FAKE, 64, FAKE, cap, 1000, FAKE, 8, 0, FAKE, None) == _lib.EINVAL
     assert g(FAKE, 0, FAKE, FAKE, 64, FAKE, cap, 1000, FAKE, 8, 0, FAKE, None) == _lib.OK
+    big = 1 << 22                                                 # ld / 128 = 32768 runs
+    assert g(FAKE, 1 << 16, FAKE, FAKE, 64, FAKE, big, 1000, FAKE, 8, 0, FAKE, None) == _lib.EINVAL   # scales
 
 
 def test_quantizers_reject_before_launch(lib):
