@@ -2,13 +2,17 @@
 //
 //   out[i, j] = sum_k A[i,k] sA(i,k) * B(j,k) sB(j,k)  (+ bias[j])
 //
-// Serves the forward (input @ weight.t()) and weight-gradient
-// (grad_output.t() @ input, both operands stored token-contiguous) call forms
-// of ColossalAI PR #6419 ("Fix: Handle LowLevelZeroPlugin with use_fp8=True",
-// "Forward pass" / "Backward pass"), for the tensorwise, rowwise, 1x128 x
-// 128x128 and 1x128 x 128x1 recipes of pytorch PR #164141 ("Add
-// _scaled_mm_v2 API") and pytorch/ao PR #2784 ("improve fp8 blockwise gemm
-// perf").
+// Serves the forward (input @ weight.t()), input-gradient (B stored [K, N])
+// and weight-gradient (grad_output.t() @ input, both operands stored
+// token-contiguous) call forms of ColossalAI PR #6419 ("Fix: Handle
+// LowLevelZeroPlugin with use_fp8=True", "Forward pass" / "Backward pass"),
+// for the tensorwise, rowwise, 1x128 x 128x128 and 1x128 x 128x1 recipes of
+// pytorch PR #164141 ("Add _scaled_mm_v2 API") and pytorch/ao PR #2784
+// ("improve fp8 blockwise gemm perf"), and MXFP8 on the block-scaled MFMA.
+// GROUPED runs the MoE form of pytorch/ao PR #4390 ("Add _grouped_mm
+// dispatch handler to Float8Tensor": expert e's rows times its own weights),
+// GROUPED_K the per-expert weight gradient (expert e's tokens as the
+// contraction); both store their outputs non-temporally.
 //
 // Schedule.  A workgroup of 8 waves (two per SIMD) computes a 256 x 256
 // output tile, each wave a 64 x 128 sub-tile: 4 x 8 fragments of

@@ -387,25 +387,42 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(
         cs[j].r = col_r[cc * 8 + j];
         cs[j].fast = cs[j].s >= kFastDivMinScale;
       }
-      // xs[i][j], y[i][j]: value and quotient of row r0 + i, column c0 + j
-      // (column scale j)
-      float xs[8][8], y[8][8];
-      const CastScale* c[8] = {&cs[0], &cs[1], &cs[2], &cs[3], &cs[4], &cs[5], &cs[6], &cs[7]};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        unpack8(v[i], xs[i]);
-        quotients8(xs[i], c, y[i]);
-      }
       if (!TRANSPOSE) {
+        // row by row: the 8 values of row r0 + i, one column scale each
+        const CastScale* c[8] = {&cs[0], &cs[1], &cs[2], &cs[3], &cs[4], &cs[5], &cs[6], &cs[7]};
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0) =
-              make_uint2(pack4(y[i], xs[i]), pack4(y[i] + 4, xs[i] + 4));
+        for (int i = 0; i < 8; ++i) {
+          float xs[8], y[8];
+          unpack8(v[i], xs);
+          quotients8(xs, c, y);
+          *reinterpret_cast<uint2*>(q + (r0 + i) * ld_q + c0) = make_uint2(pack4(y, xs), pack4(y + 4, xs + 4));
+        }
       } else {
+        // column by column: the 8 row values of column c0 + j, its scale,
+        // stored as 8 consecutive bytes of q[c0 + j, ..] (only one column's
+        // values and quotients are live at a time)
+        bool fast = true;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<uint2*>(q + (c0 + j) * ld_q + r0) =
-              make_uint2(pack4(&y[0][j], &xs[0][j], 8), pack4(&y[4][j], &xs[4][j], 8));
+        for (int j = 0; j < 8; ++j) fast = fast && cs[j].fast;
+        const bool all_fast = __all(fast);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float xc[8], yc[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t w = v[i].w[j >> 1];
+            xc[i] = bits_f32((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+          }
+          if (all_fast) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) yc[i] = div_by_scale(xc[i], cs[j].s, cs[j].r);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              yc[i] = cs[j].fast ? div_by_scale(xc[i], cs[j].s, cs[j].r) : xc[i] / cs[j].s;
+          }
+          *reinterpret_cast<uint2*>(q + (c0 + j) * ld_q + r0) = make_uint2(pack4(yc, xc), pack4(yc + 4, xc + 4));
+        }
       }
     }
     if (jt + 1 < CT) {
