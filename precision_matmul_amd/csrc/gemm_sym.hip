@@ -57,6 +57,7 @@ constexpr int SY_A = SY_BM * BK;            // A codes of one stage
 constexpr int SY_B = SY_BN * BK;            // B codes of one stage
 constexpr int SY_SCALE = 1024;              // 256 fp32 scales (sA), or up to 256 (sB)
 constexpr int SY_STAGE = SY_A + SY_B + 2 * SY_SCALE;
+constexpr int SY_GCH = 4;                   // grouped: m-tiles per XCD chunk
 constexpr int SY_TM = 64;                   // wave sub-tile
 constexpr int SY_TN = 128;
 constexpr int SY_FM = SY_TM / 16;
@@ -111,11 +112,14 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---------------- tile ----------------
-  // Grouped (MoE) problems: m-tile g of all experts (expert order) and n-tile
-  // tn go to workgroup b with b % 8 = g % 8 (workgroups are dealt to the 8
-  // XCDs round-robin), b / 8 = (g / 8) tiles_n + tn: the n-tiles of one
-  // m-tile share its A rows in one XCD's L2, and the real m-tiles (a prefix
-  // of the upper bound the grid is sized for) are spread over all XCDs.
+  // Grouped (MoE) problems: m-tiles g of all experts (expert order) go to the
+  // 8 XCDs (workgroups are dealt to them round-robin, XCD = b % 8) in chunks
+  // of SY_GCH consecutive m-tiles, chunk c to XCD c % 8; an XCD walks its
+  // m-tiles in order, all n-tiles tn of one m-tile together.  So the n-tiles
+  // of one m-tile share its A rows in one XCD's L2, the m-tiles of one expert
+  // (consecutive g) mostly share its B tiles there too, and the real m-tiles
+  // (a prefix of the upper bound the grid is sized for) are spread over all
+  // XCDs.
   // Expert e's B is [N, K] (or [K, N]) at B + e N K, its bias row e of
   // [E, N], its scales row e of [E, N] (rowwise) or grid e of [E, N/128 x
   // K/128] (128x128).
@@ -159,8 +163,9 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     K = runs * 128;
     out_off = e * p.M * p.ldo;
   } else if constexpr (GROUPED) {
-    const int r = blockIdx.x / 8;
-    const int g = (r / tiles_n) * 8 + blockIdx.x % 8;
+    const int r = blockIdx.x / 8;              // slot within the XCD
+    const int mt = r / tiles_n;                // the XCD's m-tile ordinal
+    const int g = ((mt / SY_GCH) * 8 + int(blockIdx.x % 8)) * SY_GCH + mt % SY_GCH;
     tn = r % tiles_n;
     if (g >= tiles_m) return;
     int e = 0;
@@ -684,8 +689,10 @@ hipError_t launch_sym(const GemmProblem& p, hipStream_t st) {
   const int tiles_n = int((p.N + SY_BN - 1) / SY_BN);
   const int64_t tiles = int64_t(tiles_m) * tiles_n;
   if (tiles == 0) return hipSuccess;
-  // grouped: whole groups of 8 m-tiles (see the tile order in the kernel)
-  const int grid = GROUPED ? int((tiles_m + 7) / 8 * 8 * tiles_n) : int((tiles + 7) / 8 * 8);
+  // grouped: whole rounds of 8 chunks of SY_GCH m-tiles (see the tile order
+  // in the kernel)
+  const int grid = GROUPED ? int((tiles_m + 8 * SY_GCH - 1) / (8 * SY_GCH) * (8 * SY_GCH) * tiles_n)
+                           : int((tiles + 7) / 8 * 8);
   const int outb = OUT_BF16 ? 2 : 4;
   const int vec_out = ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0) && ((p.ldo * outb) % 16 == 0);
   // blockwise and MXFP8 problems have K % 128 == 0 (checked by the caller)
