@@ -242,3 +242,31 @@ def test_grouped_weight_gradient_moe_shape():
     rqx2, rsx2, _ = quant.quantize_grouped_128x1(x[rows], sub)
     ref = gemm.grouped_grad_weight(rqg2, rsg2, rqx2, rsx2, sub, out_dtype=None)
     _assert_close(out[pick], ref[pick], "grouped grad_weight MoE shape, 6 experts")
+
+
+def test_grouped_all_experts_empty():
+    """Offsets all zero: the grouped GEMM writes no row, the per-expert
+    weight gradient writes zeros for every expert, the quantizer no run."""
+    E, N, K, T = 4, 256, 256, 37
+    g = workloads.streams(99, 3)
+    act = workloads.normal_bf16(g[0], (T, K))
+    W = workloads.normal_bf16(g[1], (E, N, K), 0.02)
+    go = workloads.normal_bf16(g[2], (T, N), 1e-3)
+    offs = _offs_dev(np.zeros(E, np.int32))
+    qa, sa = fp8mm.fp8_quantize_blockwise(bf16_dev(act), (1, 128))
+    qw, sw = fp8mm.fp8_quantize_blockwise(bf16_dev(W.reshape(E * N, K)), (128, 128))
+    out = torch.full((T, N), 3.0, dtype=torch.bfloat16, device="cuda")
+    fp8mm.fp8_scaled_grouped_mm_v2(qa, qw.view(E, N, K), offs, sa, "1x128", sw.view(E, N // 128, K // 128),
+                                   "128x128", out=out)
+    assert bool((out == 3.0).all()), "no row belongs to an expert"
+    qg, sg = fp8mm.fp8_quantize_grouped_128x1(bf16_dev(go), offs)
+    qx, sx = fp8mm.fp8_quantize_grouped_128x1(bf16_dev(act), offs)
+    gw = fp8mm.fp8_grouped_linear_grad_weight(qg, sg, qx, sx, offs, T, out_dtype=torch.float32)
+    assert gw.shape == (E, N, K) and not bool(gw.any())
+
+
+def test_grouped_weight_gradient_runs_of_exactly_128_and_single_tokens():
+    got, ref = _grouped_grad_weight_case(np.array([128, 1, 256, 0, 1, 127]), 128, 256, seed=5,
+                                         out_dtype=torch.bfloat16)
+    assert not got[3].any()
+    _assert_close(got, ref, "grouped grad_weight whole and single-token runs")
