@@ -332,13 +332,13 @@ def time_graph(torch, fn, calls=10, iters=20):
 
 
 def cpu_baseline(workloads):
-    """The oracle (untuned numpy + OpenBLAS float64) on a bounded sample of the
-    default workload: rows [0, 12480) of the 16640x5120x8192 blockwise forward
-    step (quantize those input rows and the full weight, then the GEMM)."""
+    """The oracle (untuned numpy + OpenBLAS float64) on the default workload:
+    the whole 16640x5120x8192 blockwise forward step (quantize the input and
+    the weight, then the GEMM), about 10-15 s on the host's cores."""
     from oracle import gemm as ogemm
     from oracle import quant as oquant
 
-    Ms, N, K = 12480, 5120, 8192
+    Ms, N, K = 16640, 5120, 8192
     inp = workloads.blockwise(M=16640, N=N, K=K)
     x = inp["input"][:Ms]
     w = inp["weight"]
@@ -355,9 +355,9 @@ def cpu_baseline(workloads):
         threads = cores
     return {"value": round(2.0 * Ms * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(min(cores, threads)),
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"rows 0..{Ms} of the blockwise 1x128_128x128 forward step at 16640x5120x8192: "
-                      f"numpy oracle quantization of those input rows and the whole weight, float64 GEMM "
-                      f"({2.0 * Ms * N * K / 1e9:.0f} GFLOP), rounding to bf16"}
+            "sample": f"the whole blockwise 1x128_128x128 forward step at {Ms}x{N}x{K}: numpy oracle "
+                      f"quantization of the input and the weight, float64 GEMM ({2.0 * Ms * N * K / 1e9:.0f} "
+                      f"GFLOP), rounding to bf16"}
 
 
 GEMM_SOURCES = ("gemm.hip", "gemm_sym.hip", "gemm_common.hpp", "grouped.hpp", "launch.hpp")
