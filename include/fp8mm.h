@@ -272,6 +272,21 @@ fp8mm_status fp8_quantize_grouped_128x1(const void* x, int64_t T, int64_t C,
                                         int64_t E, uint8_t* q_t, int64_t ld_q,
                                         float* scale, hipStream_t stream);
 
+/* One read of x, both layouts the MoE layer needs of it (the grouped form
+ * of fp8_quantize_blockwise_dual): the 1x128 codes q_row [T, ld_q_row] with
+ * scales scale_row [C/128, T] (as fp8_quantize_blockwise with block (1, 128))
+ * of every row an expert owns, and the per-expert runs q_t / scale_t exactly
+ * as fp8_quantize_grouped_128x1 writes them.  C % 128 == 0, ld_q_row >= C
+ * and a multiple of 16; rows at or past offsets[E-1] are left unwritten in
+ * q_row and scale_row.  Other arguments and errors as
+ * fp8_quantize_grouped_128x1. */
+fp8mm_status fp8_quantize_grouped_dual(const void* x, int64_t T, int64_t C,
+                                       int64_t ld_x, const int32_t* offsets,
+                                       int64_t E, uint8_t* q_row,
+                                       int64_t ld_q_row, float* scale_row,
+                                       uint8_t* q_t, int64_t ld_q,
+                                       float* scale_t, hipStream_t stream);
+
 /* grad_w bf16 or fp32 [E, N_out, K_in] (dense) from the two quantizer
  * outputs of the same offsets, T and ld:
  *   gt_q uint8 [N_out, ld], gt_scale float32 [ld/128, N_out]: grad_output

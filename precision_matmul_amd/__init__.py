@@ -20,7 +20,8 @@ from . import _lib
 __all__ = [
     "fp8_quantize_tensorwise", "fp8_quantize_rowwise", "fp8_quantize_blockwise", "fp8_quantize_blockwise_dual", "fp8_quantize_mx",
     "fp8_scaled_mm", "fp8_scaled_grouped_mm", "fp8_scaled_grouped_mm_v2", "grouped_runs_capacity",
-    "fp8_quantize_grouped_128x1", "fp8_grouped_linear_grad_weight", "fp8_linear_forward",
+    "fp8_quantize_grouped_128x1", "fp8_quantize_grouped_dual", "fp8_grouped_linear_grad_weight",
+    "fp8_linear_forward",
     "fp8_linear_grad_input", "fp8_linear_grad_weight", "recipe_pair_supported",
     "FP8BlockwiseLinear", "fp8_blockwise_linear", "FP8GroupedLinear", "fp8_grouped_linear",
 ]
@@ -316,6 +317,30 @@ def fp8_quantize_grouped_128x1(x, offsets):
                                                 q.data_ptr(), q.stride(0), scale.data_ptr(), _stream(x))
     _lib.check(st, "fp8_quantize_grouped_128x1")
     return q, scale
+
+
+def fp8_quantize_grouped_dual(x, offsets):
+    """x bf16 [T, C] (C % 128 == 0) -> (q_row uint8 [T, C], scale_row float32
+    [C/128, T], q_t uint8 [C, ld], scale_t float32 [ld/128, C]) from one read:
+    the 1x128 codes of every row an expert owns (rows at or past
+    offsets[-1] are left unwritten) and the per-expert runs of
+    fp8_quantize_grouped_128x1."""
+    _need(x, torch.bfloat16, "x")
+    _need(offsets, torch.int32, "offsets")
+    if not offsets.is_contiguous() or offsets.dim() != 1:
+        raise ValueError("offsets must be a contiguous 1-D int32 tensor")
+    T, C = x.shape
+    E = offsets.numel()
+    ld = 128 * grouped_runs_capacity(T, E)
+    q_row = torch.empty((T, C), dtype=torch.uint8, device=x.device)
+    s_row = torch.empty((C // 128, T), dtype=torch.float32, device=x.device)
+    q_t = torch.empty((C, max(ld, 16)), dtype=torch.uint8, device=x.device)
+    s_t = torch.empty((ld // 128, C), dtype=torch.float32, device=x.device)
+    st = _lib.load().fp8_quantize_grouped_dual(x.data_ptr(), T, C, _ld(x, "x"), offsets.data_ptr(), E,
+                                               q_row.data_ptr(), _ld16(C), s_row.data_ptr(), q_t.data_ptr(),
+                                               q_t.stride(0), s_t.data_ptr(), _stream(x))
+    _lib.check(st, "fp8_quantize_grouped_dual")
+    return q_row, s_row, q_t, s_t
 
 
 def fp8_grouped_linear_grad_weight(gt_q, gt_scale, xt_q, xt_scale, offsets, T, out_dtype=torch.bfloat16):

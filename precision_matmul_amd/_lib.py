@@ -31,6 +31,7 @@ SIGNATURES = {
     "fp8_scaled_grouped_mm_v2": (_i, [_p, _i64, _i64, _p, _i64, _i64, _i, _p, _p, _i, _p, _i, _p, _i, _p, _i64, _p]),
     "fp8mm_grouped_runs_capacity": (_i64, [_i64, _i64]),
     "fp8_quantize_grouped_128x1": (_i, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p]),
+    "fp8_quantize_grouped_dual": (_i, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _p]),
     "fp8_grouped_linear_grad_weight": (_i, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _p, _i64, _i, _p, _p]),
     "fp8_linear_forward": (_i, [_p, _i64, _i64, _p, _i, _p, _i64, _p, _i, _p, _i, _p, _p]),
     "fp8_linear_grad_input": (_i, [_p, _i64, _i64, _p, _i, _p, _i64, _p, _i, _i, _p, _p]),

@@ -14,6 +14,7 @@
 
 #include "fp8mm.h"
 #include "launch.hpp"
+#include "quant_launch.hpp"
 
 namespace {
 
@@ -352,8 +353,32 @@ fp8mm_status fp8_quantize_grouped_128x1(const void* x, int64_t T, int64_t C, int
   if (T == 0 || C == 0 || E == 0) return ok();
   if (!scale) return fail(FP8MM_EINVAL, "scale must not be NULL");
   return from_hip(fp8mm::launch_quant_grouped_128x1(static_cast<const uint16_t*>(x), T, C, ld_x, offsets, E, q_t,
-                                                    ld_q, scale, stream),
+                                                    ld_q, scale, nullptr, 0, nullptr, stream),
                   "fp8_quantize_grouped_128x1");
+}
+
+fp8mm_status fp8_quantize_grouped_dual(const void* x, int64_t T, int64_t C, int64_t ld_x, const int32_t* offsets,
+                                       int64_t E, uint8_t* q_row, int64_t ld_q_row, float* scale_row, uint8_t* q_t,
+                                       int64_t ld_q, float* scale_t, hipStream_t stream) {
+  fp8mm_status st = check_quant_common(x, T, C, ld_x, q_t, scale_t);
+  if (st != FP8MM_OK) return st;
+  if (E < 0 || E > (int64_t(1) << 20)) return fail(FP8MM_EINVAL, "E (%lld) must be in [0, 2^20]", (long long)E);
+  if (!offsets && E > 0) return fail(FP8MM_EINVAL, "offsets are required");
+  if (C % 128 != 0) return fail(FP8MM_EINVAL, "C (%lld) must be a multiple of 128", (long long)C);
+  const int64_t runs = T / 128 + E;
+  if (ld_q < 128 * runs || ld_q % 16 != 0 || ld_q > kMaxLd)
+    return fail(FP8MM_EINVAL, "ld_q (%lld) must be >= 128 (T/128 + E) = %lld, a multiple of 16 and <= 2^22",
+                (long long)ld_q, (long long)(128 * runs));
+  if (ld_q_row < C || ld_q_row % 16 != 0 || ld_q_row > kMaxLd)
+    return fail(FP8MM_EINVAL, "ld_q_row (%lld) must be >= C (%lld), a multiple of 16 and <= 2^22",
+                (long long)ld_q_row, (long long)C);
+  if (C / 128 + 1 > 65535) return fail(FP8MM_EINVAL, "C (%lld) must be below 128 x 65535", (long long)C);
+  if (T == 0 || C == 0 || E == 0) return ok();
+  if (!q_row || !scale_row || !scale_t) return fail(FP8MM_EINVAL, "null pointer argument (q_row, scale_row, scale_t)");
+  if (!aligned16(q_row)) return fail(FP8MM_EINVAL, "q_row must be 16-byte aligned");
+  return from_hip(fp8mm::launch_quant_grouped_128x1(static_cast<const uint16_t*>(x), T, C, ld_x, offsets, E, q_t,
+                                                    ld_q, scale_t, q_row, ld_q_row, scale_row, stream),
+                  "fp8_quantize_grouped_dual");
 }
 
 fp8mm_status fp8_grouped_linear_grad_weight(const uint8_t* gt_q, int64_t N_out, const float* gt_scale,

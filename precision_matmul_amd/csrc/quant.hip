@@ -13,7 +13,7 @@
 // reductions are integer max operations and are exact and order-free.
 #include "fp8_codec.hpp"
 #include "grouped.hpp"
-#include "launch.hpp"
+#include "quant_launch.hpp"
 
 namespace fp8mm {
 namespace {
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale,
     uint8_t* __restrict__ q_row, int64_t ld_q_row, float* __restrict__ scale_row,
     const int32_t* __restrict__ offsets, int64_t E) {
-  static_assert(!GROUPED || (TRANSPOSE && !DUAL), "grouped runs: transposed codes only");
+  static_assert(!GROUPED || TRANSPOSE, "grouped runs: transposed codes only");
   constexpr int CT = GROUPED ? kGroupedColTiles : 1;
   __shared__ U16x8 colmax[4][16];
   __shared__ float col_s[128];
@@ -371,13 +371,16 @@ __global__ __launch_bounds__(256) void quant_128x1_kernel(
     if (active) {
       if constexpr (DUAL) {
         // 1x128 of the tile's rows: each row's 128 columns are held by the 16
-        // consecutive lanes of one row group (cols % 128 == 0: every tile full)
+        // consecutive lanes of one row group (cols % 128 == 0: every tile
+        // full); grouped, only the run's rows of x (a row group is all in or
+        // all out, so the 16-lane reduction stays whole)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+          if (GROUPED && rg * 8 + i >= rows_here) continue;
           const uint32_t mr = group16_max(absmax8(v[i]));
           const float sr = scale_from_amax(bf16_to_f32(uint16_t(mr)), 0.0f, false);
-          if (cc == 0) scale_row[tile * rows + r0 + i] = sr;
-          *reinterpret_cast<uint2*>(q_row + (r0 + i) * ld_q_row + c0) = cast8(v[i], make_cast_scale(sr));
+          if (cc == 0) scale_row[tile * rows + xr0 + i] = sr;
+          *reinterpret_cast<uint2*>(q_row + (xr0 + i) * ld_q_row + c0) = cast8(v[i], make_cast_scale(sr));
         }
       }
       CastScale cs[8];
@@ -636,14 +639,18 @@ hipError_t launch_quant_blockwise_dual(const uint16_t* x, int64_t rows, int64_t 
 
 hipError_t launch_quant_grouped_128x1(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                       const int32_t* offsets, int64_t E, uint8_t* q_t, int64_t ld_q, float* scale,
-                                      hipStream_t st) {
+                                      uint8_t* q_row, int64_t ld_q_row, float* scale_row, hipStream_t st) {
   if (rows == 0 || cols == 0 || E == 0) return hipSuccess;
   // an upper bound on the run count: each expert adds at most one short run
   const int64_t runs_max = rows / 128 + E;
   const int64_t tiles = (cols + 127) / 128;
   const dim3 grid(unsigned(runs_max), unsigned((tiles + kGroupedColTiles - 1) / kGroupedColTiles));
-  hipLaunchKernelGGL((quant_128x1_kernel<true, false, true>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q_t, ld_q,
-                     scale, nullptr, int64_t(0), nullptr, offsets, E);
+  if (q_row)
+    hipLaunchKernelGGL((quant_128x1_kernel<true, true, true>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q_t, ld_q,
+                       scale, q_row, ld_q_row, scale_row, offsets, E);
+  else
+    hipLaunchKernelGGL((quant_128x1_kernel<true, false, true>), grid, dim3(256), 0, st, x, rows, cols, ld_x, q_t,
+                       ld_q, scale, nullptr, int64_t(0), nullptr, offsets, E);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ import torch
 
 from . import (fp8_grouped_linear_grad_weight, fp8_linear_forward, fp8_linear_grad_input, fp8_linear_grad_weight,
                fp8_quantize_blockwise, fp8_quantize_blockwise_dual, fp8_quantize_grouped_128x1,
-               fp8_scaled_grouped_mm_v2)
+               fp8_quantize_grouped_dual, fp8_scaled_grouped_mm_v2)
 
 
 class FP8BlockwiseLinear(torch.autograd.Function):
@@ -65,11 +65,11 @@ class FP8GroupedLinear(torch.autograd.Function):
     expert e owning token rows [offs[e-1], offs[e]) (the grouped form of
     pytorch/ao PR #4390), in the blockwise recipe applied per expert:
 
-      forward:  x -> 1x128 codes (forward GEMM) and per-expert 128-token runs
-                     written transposed (kept for grad_weight)
+      forward:  x -> one read: 1x128 codes (forward GEMM) and per-expert
+                     128-token runs written transposed (kept for grad_weight)
                 w [E, N_out, K_in] -> 128x128 codes per expert (kept)
                 y = grouped GEMM, expert weights read [N, K]
-      backward: grad_out -> 1x128 codes and per-expert runs
+      backward: grad_out -> one read: 1x128 codes and per-expert runs
                 grad_x    = grouped GEMM, the same weight codes read [K, N]
                 grad_w[e] = grad_out[rows_e].t() @ x[rows_e]
 
@@ -83,8 +83,7 @@ class FP8GroupedLinear(torch.autograd.Function):
         x = x.contiguous()
         w = w.contiguous()
         E, N_out, K_in = w.shape
-        qx, sx = fp8_quantize_blockwise(x, (1, 128))
-        qxt, sxt = fp8_quantize_grouped_128x1(x, offs)
+        qx, sx, qxt, sxt = fp8_quantize_grouped_dual(x, offs)
         qw, sw = fp8_quantize_blockwise(w.view(E * N_out, K_in), (128, 128))
         qw = qw.view(E, N_out, K_in)
         sw = sw.view(E, N_out // 128, K_in // 128)
@@ -97,11 +96,16 @@ class FP8GroupedLinear(torch.autograd.Function):
         qxt, sxt, qw, sw, offs = ctx.saved_tensors
         g = grad_out.to(torch.bfloat16).contiguous()
         grad_x = grad_w = None
-        if ctx.needs_input_grad[0]:
+        need_x, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if need_x and need_w:
+            qg, sg, qgt, sgt = fp8_quantize_grouped_dual(g, offs)
+        elif need_x:
             qg, sg = fp8_quantize_blockwise(g, (1, 128))
-            grad_x = fp8_scaled_grouped_mm_v2(qg, qw, offs, sg, "1x128", sw, "128x128", b_layout="KN")
-        if ctx.needs_input_grad[1]:
+        elif need_w:
             qgt, sgt = fp8_quantize_grouped_128x1(g, offs)
+        if need_x:
+            grad_x = fp8_scaled_grouped_mm_v2(qg, qw, offs, sg, "1x128", sw, "128x128", b_layout="KN")
+        if need_w:
             grad_w = fp8_grouped_linear_grad_weight(qgt, sgt, qxt, sxt, offs, ctx.tokens)
         return grad_x, grad_w, None
 

@@ -270,3 +270,23 @@ def test_grouped_weight_gradient_runs_of_exactly_128_and_single_tokens():
                                          out_dtype=torch.bfloat16)
     assert not got[3].any()
     _assert_close(got, ref, "grouped grad_weight whole and single-token runs")
+
+
+@pytest.mark.parametrize("sizes,C", [([130, 5, 0, 257, 1, 128, 0, 300], 128), ([700, 40], 256), ([0, 0], 128)])
+def test_grouped_dual_quant_bit_exact(sizes, C):
+    """One read, both layouts: the 1x128 codes of every owned row and the
+    per-expert runs, each bit-exact against the oracle."""
+    offs = np.cumsum(sizes).astype(np.int32)
+    T = int(offs[-1]) + 3                                       # 3 trailing rows no expert owns
+    x = workloads.normal_bf16(workloads.streams(len(sizes) + 7 * C, 1)[0], (T, C), 2.0)
+    say(f"grouped dual quant sizes={sizes} C={C}")
+    q_row, s_row, q_t, s_t = fp8mm.fp8_quantize_grouped_dual(bf16_dev(x), _offs_dev(offs))
+    M = int(offs[-1])
+    if M:
+        rq, rs = quant.quantize_blockwise(x[:M], 1, 128)
+        assert np.array_equal(host(q_row)[:M], rq), "1x128 codes of the owned rows"
+        assert np.array_equal(host(s_row)[:, :M], rs), "1x128 scales of the owned rows"
+    rq, rs, _ = quant.quantize_grouped_128x1(x, offs)
+    nb = rs.shape[0]
+    assert np.array_equal(host(q_t)[:, :128 * nb], rq), "runs"
+    assert np.array_equal(host(s_t)[:nb], rs), "run scales"

@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -156,6 +156,18 @@ def test_grouped_weight_gradient_entries_check_capacity(lib):
     assert g(FAKE, 0, FAKE, FAKE, 64, FAKE, cap, 1000, FAKE, 8, 0, FAKE, None) == _lib.OK
     big = 1 << 22                                                 # ld / 128 = 32768 runs
     assert g(FAKE, 1 << 16, FAKE, FAKE, 64, FAKE, big, 1000, FAKE, 8, 0, FAKE, None) == _lib.EINVAL   # scales
+
+
+def test_grouped_dual_quantizer_rejects_before_launch(lib):
+    d = lib.fp8_quantize_grouped_dual
+    cap = 128 * (1000 // 128 + 8)
+    # x, T, C, ld_x, offsets, E, q_row, ld_q_row, scale_row, q_t, ld_q, scale_t, stream
+    assert d(FAKE, 1000, 64, 64, FAKE, 8, FAKE, 64, FAKE, FAKE, cap, FAKE, None) == _lib.EINVAL      # C % 128
+    assert d(FAKE, 1000, 128, 128, FAKE, 8, FAKE, 112, FAKE, FAKE, cap, FAKE, None) == _lib.EINVAL   # ld_q_row
+    assert d(FAKE, 1000, 128, 128, FAKE, 8, None, 128, FAKE, FAKE, cap, FAKE, None) == _lib.EINVAL   # q_row NULL
+    assert d(FAKE, 1000, 128, 128, FAKE, 8, FAKE + 8, 128, FAKE, FAKE, cap, FAKE, None) == _lib.EINVAL
+    assert d(FAKE, 1000, 128, 128, FAKE, 8, FAKE, 128, FAKE, FAKE, cap - 128, FAKE, None) == _lib.EINVAL
+    assert d(FAKE, 1000, 128, 128, None, 8, FAKE, 128, FAKE, FAKE, cap, FAKE, None) == _lib.EINVAL   # offsets
 
 
 def test_quantizers_reject_before_launch(lib):
