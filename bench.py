@@ -397,7 +397,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the library is a single-GPU kernel library; see DESIGN.md for how it would shard)",
+              "(the library is a single-GPU kernel library with no collectives)",
               file=sys.stderr, flush=True)
         sys.exit(2)
 
