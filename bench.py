@@ -575,9 +575,9 @@ def main():
             "shape_T_Kin_Nout_E": [Tg, K_, N_, E_], "ms": round(m_med, 4),
             "ms_min_max": [round(m_min, 4), round(m_max, 4)],
             "tflops": round(m_flops / (m_med * 1e-3) / 1e12, 2),
-            "step": "1x128 and per-expert 128x1 quantize of x, 128x128 quantize of the expert weights, grouped "
-                    "forward; 1x128 and per-expert 128x1 quantize of grad_output, grouped input gradient, "
-                    "per-expert weight gradient"}
+            "step": "dual-layout (1x128 + per-expert runs) quantize of x, 128x128 quantize of the expert weights, "
+                    "grouped forward; dual-layout quantize of grad_output, grouped input gradient, per-expert "
+                    "weight gradient"}
         del xg, wg, gg, og
         torch.cuda.empty_cache()
 
