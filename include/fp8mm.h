@@ -201,8 +201,11 @@ fp8mm_status fp8_scaled_mm(const uint8_t* A, int64_t M, int64_t K, int64_t lda,
  *   out: [M_total, N], leading dimension ldo >= N.  Rows at or past
  *     offsets[E-1] are not written.
  * Offsets are read on the device only; they are not validated on the host
- * (that would need a synchronization).  The kernels clamp them to
- * [0, M_total] and treat a decreasing pair as an empty group.
+ * (that would need a synchronization) and must be non-decreasing.  The
+ * kernels clamp each to [0, M_total] and treat a decreasing pair as an empty
+ * group, so no access leaves the arrays; the next expert then starts at the
+ * smaller offset, and rows that two experts cover are written twice (their
+ * values are undefined).
  * K % 16 == 0. */
 fp8mm_status fp8_scaled_grouped_mm(const uint8_t* A, int64_t M_total,
                                    int64_t K, const uint8_t* B_EnK, int64_t E,
