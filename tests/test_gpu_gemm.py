@@ -406,3 +406,65 @@ def test_full_grouped_moe_sampled():
         ref.append(gemm.scaled_mm(ra[t:t + 1], rw, rsa[t:t + 1], "rowwise", rsw, "rowwise", out_dtype=None)[0])
         got.append(out[r, cols])
     _assert_close(np.array(got), np.array(ref), "grouped E=64 16384x1408x2048 sampled")
+
+
+def _random_case(rng):
+    """One seeded random GEMM: recipe pair, B layout, ragged sizes within the
+    ABI's rules, output dtype and bias."""
+    recipe = rng.choice(["tensorwise", "rowwise", "1x128_128x128", "1x128_128x1", "mxfp8"])
+    layout = "NK" if recipe in ("mxfp8", "1x128_128x1") or rng.random() < 0.5 else "KN"
+    blocked = recipe in ("1x128_128x128", "1x128_128x1", "mxfp8")
+    M = int(rng.integers(1, 1500))
+    K = int(rng.integers(1, 9)) * 128 if blocked else int(rng.integers(1, 64)) * 16
+    if recipe == "1x128_128x128":
+        N = int(rng.integers(1, 10)) * 128
+    elif layout == "KN" or recipe == "1x128_128x1":
+        N = int(rng.integers(1, 80)) * 16
+    else:
+        N = int(rng.integers(1, 1300))
+    out_dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    with_bias = recipe in ("tensorwise", "rowwise") and rng.random() < 0.5
+    return recipe, layout, M, N, K, out_dtype, with_bias
+
+
+def test_random_shapes_sweep():
+    """40 seeded random problems through every dispatch path the sizes reach
+    (small problems, the streaming kernel with or without a row tail), each
+    against the oracle on the same bf16 inputs."""
+    rng = np.random.default_rng(20260101)
+    for case in range(40):
+        recipe, layout, M, N, K, out_dtype, with_bias = _random_case(rng)
+        say(f"sweep {case}: {recipe} {layout} M={M} N={N} K={K} {out_dtype} bias={with_bias}")
+        g = workloads.streams(1000 + case, 3)
+        x = workloads.normal_bf16(g[0], (M, K))
+        w = workloads.normal_bf16(g[1], (N, K), 0.02)            # logical [N, K]
+        bias = workloads.normal_bf16(g[2], (N,), 0.5) if with_bias else None
+        if recipe in ("tensorwise", "rowwise"):
+            qa, sa, ra, rsa = _quant_both(x, recipe)
+            qb, sb, rb, rsb = _quant_both(w, recipe)
+            rec_a = rec_b = recipe
+            if layout == "KN":                                   # codes stored [K, N], same scales
+                qb, rb = qb.t().contiguous(), np.ascontiguousarray(rb.T)
+            if recipe == "rowwise":
+                sa, sb = sa.reshape(-1), sb.reshape(-1)
+        elif recipe == "1x128_128x128":
+            qa, sa, ra, rsa = _quant_both(x, "1x128")
+            stored = w if layout == "NK" else np.ascontiguousarray(w.T)
+            qb, sb, rb, rsb = _quant_both(stored, "128x128")
+            rec_a, rec_b = "1x128", "128x128"
+        elif recipe == "1x128_128x1":
+            qa, sa, ra, rsa = _quant_both(x, "1x128")
+            qb, sb, rb, rsb = _quant_both(np.ascontiguousarray(w.T), "128x1", transpose_out=True)
+            rec_a, rec_b = "1x128", "128x1"
+        else:
+            qa, sa = fp8mm.fp8_quantize_mx(bf16_dev(x))
+            qb, sb = fp8mm.fp8_quantize_mx(bf16_dev(w))
+            ra, rsa = mx.quantize_mx(x)
+            rb, rsb = mx.quantize_mx(w)
+            rec_a = rec_b = "mxfp8"
+        out = fp8mm.fp8_scaled_mm(qa, qb, sa, rec_a, sb, rec_b, b_layout=layout, out_dtype=out_dtype,
+                                  bias=None if bias is None else bf16_dev(bias))
+        ref = gemm.scaled_mm(ra, rb, rsa, rec_a, rsb, rec_b, layout,
+                             bias=None if bias is None else quant.bf16_to_f32(bias), out_dtype=None)
+        _assert_close(out_f64(out), ref, f"sweep {case} {recipe} {layout} {M}x{N}x{K}",
+                      out_dtype="bf16" if out_dtype == torch.bfloat16 else "fp32")
