@@ -290,3 +290,50 @@ def test_grouped_dual_quant_bit_exact(sizes, C):
     nb = rs.shape[0]
     assert np.array_equal(host(q_t)[:, :128 * nb], rq), "runs"
     assert np.array_equal(host(s_t)[:nb], rs), "run scales"
+
+
+def test_grouped_random_sweep():
+    """Seeded random grouped problems: expert count and sizes (empty experts
+    included), recipe, weight layout, N and K within the ABI's rules; the
+    grouped GEMM and the per-expert weight gradient against the oracle."""
+    rng = np.random.default_rng(20260202)
+    for case in range(16):
+        E = int(rng.integers(1, 13))
+        sizes = rng.integers(0, 400, size=E) * (rng.random(E) > 0.2)
+        blockwise = bool(rng.random() < 0.5)
+        layout = "NK" if rng.random() < 0.5 else "KN"
+        K = int(rng.integers(1, 7)) * 128
+        N = int(rng.integers(1, 5)) * 128 if blockwise else int(rng.integers(1, 40)) * 16
+        say(f"grouped sweep {case}: E={E} sizes={[int(v) for v in sizes]} {'blockwise' if blockwise else 'rowwise'} "
+            f"{layout} N={N} K={K}")
+        if blockwise:
+            got, ref = _grouped_blockwise_case(E, N, K, np.array(sizes), layout, seed=300 + case)
+        else:
+            offs = np.cumsum(sizes).astype(np.int32)
+            g = workloads.streams(300 + case, 2)
+            act = workloads.normal_bf16(g[0], (int(offs[-1]) + 2, K))
+            W = workloads.normal_bf16(g[1], (E * N, K), 0.02)
+            qa, sa = fp8mm.fp8_quantize_rowwise(bf16_dev(act))
+            ra, rsa = quant.quantize_rowwise(act)
+            qw, sw = fp8mm.fp8_quantize_rowwise(bf16_dev(W))
+            rw, rsw = quant.quantize_rowwise(W)
+            qwe, rwe = qw.view(E, N, K), rw.reshape(E, N, K)
+            if layout == "KN":
+                qwe, rwe = qwe.transpose(1, 2).contiguous(), np.ascontiguousarray(rwe.transpose(0, 2, 1))
+            out = fp8mm.fp8_scaled_grouped_mm_v2(qa, qwe, _offs_dev(offs), sa.reshape(-1), "rowwise",
+                                                 sw.reshape(-1), "rowwise", b_layout=layout)
+            ref, written = gemm.grouped_mm(ra, rwe, offs, rsa, rsw.reshape(E, N), out_dtype=None, layout=layout)
+            g_all = out_f64(out)
+            assert not g_all[~written].any()
+            got, ref = g_all[written], ref[written]
+        if got.size:
+            _assert_close(got, ref, f"grouped sweep {case}")
+        # the per-expert weight gradient on the same routing
+        N_out, K_in = int(rng.integers(1, 20)) * 16, int(rng.integers(1, 20)) * 16
+        gw, rgw = _grouped_grad_weight_case(np.array(sizes), N_out, K_in, seed=400 + case,
+                                            out_dtype=torch.float32 if case % 2 else torch.bfloat16)
+        for e, m in enumerate(sizes):
+            if m == 0:
+                assert not gw[e].any()
+        if np.abs(rgw).max() > 0:
+            _assert_close(gw, rgw, f"grouped grad_weight sweep {case}", out_dtype="fp32" if case % 2 else "bf16")
