@@ -451,6 +451,11 @@ def main():
           flush=True)
 
     traffic, call_kernels = measured_profile(args.workload)
+    # The pages' own GEMM-only figures for these shapes (pytorch/ao PR #2784,
+    # "improve fp8 blockwise gemm perf", the two tables; hardware not named):
+    # context for the GEMM alone, not for the step `value`.
+    pages_gemm = {"blockwise_fwd_16640x5120x8192": 1008.91, "blockwise_fwd_16640x8192x5120": 1002.23,
+                  "blockwise_grad_weight_5120x8192x16640": 808.271}.get(args.workload)
 
     result = {
         "metric": "FP8 scaled-GEMM TFLOP/s at 1 MI355X + % of FP8 MFMA peak, per recipe",
@@ -472,6 +477,11 @@ def main():
                      "frac": round(achieved / FP8_DENSE_PEAK_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_bytes": wl["gemm_bytes"], "gemm_ms": round(gemm_ms, 4)},
     }
+    if pages_gemm is not None:
+        result["context_pages_gemm"] = {
+            "tflops": pages_gemm, "hardware": "not named on the page",
+            "gemm_over_pages": round(achieved / pages_gemm, 3),
+            "note": "the pages time the GEMM alone; value above is the whole step (quantize + GEMM)"}
 
     if not args.no_recipes:
         copy_gbs = copy_ceiling_gbps(torch)
