@@ -304,3 +304,67 @@ def test_full_size_rowwise_moe_weights_sampled_rows():
     rows = np.random.default_rng(2).choice(W.shape[0], 256, replace=False)
     rq, rs = quant.quantize_rowwise(W[rows])
     assert np.array_equal(qh[rows], rq) and np.array_equal(sh[rows, 0], rs)
+
+
+def test_quantizer_random_sweep():
+    """Seeded random shapes and magnitudes through every quantizer entry
+    point, each bit-exact against the oracle.  Rows mix scales 2^-30 .. 2^30,
+    and an x with ld_x > cols exercises the strided read."""
+    rng = np.random.default_rng(20260303)
+    kinds = ["tensorwise", "rowwise", "1x128", "128x128", "128x1", "128x1T", "dual", "mx", "grouped",
+             "grouped_dual"]
+    for case in range(30):
+        kind = kinds[case % len(kinds)]
+        if kind in ("128x128", "128x1", "128x1T", "dual"):
+            rows = int(rng.integers(1, 6)) * 128
+        else:
+            rows = int(rng.integers(1, 700))
+        if kind in ("1x128", "128x128", "dual", "grouped_dual"):
+            cols = int(rng.integers(1, 9)) * 128
+        elif kind == "mx":
+            cols = int(rng.integers(1, 40)) * 32
+        else:
+            cols = int(rng.integers(1, 80)) * 16
+        pad = int(rng.integers(0, 3)) * 8
+        scale_rows = np.exp2(rng.integers(-30, 30, size=(rows, 1))).astype(np.float32)
+        full = workloads.f32_to_bf16_bits((rng.standard_normal((rows, cols + pad)) * scale_rows).astype(np.float32))
+        x = np.ascontiguousarray(full[:, :cols])
+        xd = bf16_dev(full)[:, :cols]                     # leading dimension cols + pad
+        say(f"quant sweep {case}: {kind} {rows}x{cols} ld={cols + pad}")
+        what = f"quant sweep {case} {kind} {rows}x{cols}"
+        if kind == "tensorwise":
+            _check(*fp8mm.fp8_quantize_tensorwise(xd), *quant.quantize_tensorwise(x), what)
+        elif kind == "rowwise":
+            _check(*fp8mm.fp8_quantize_rowwise(xd), *quant.quantize_rowwise(x), what)
+        elif kind in ("1x128", "128x128", "128x1"):
+            blk = {"1x128": (1, 128), "128x128": (128, 128), "128x1": (128, 1)}[kind]
+            _check(*fp8mm.fp8_quantize_blockwise(xd, blk), *quant.quantize_blockwise(x, *blk), what)
+        elif kind == "128x1T":
+            _check(*fp8mm.fp8_quantize_blockwise(xd, (128, 1), transpose_out=True),
+                   *quant.quantize_blockwise(x, 128, 1, transpose_out=True), what)
+        elif kind == "dual":
+            q_row, s_row, q_col, s_col = fp8mm.fp8_quantize_blockwise_dual(xd)
+            _check(q_row, s_row, *quant.quantize_blockwise(x, 1, 128), what + " rows")
+            _check(q_col, s_col, *quant.quantize_blockwise(x, 128, 1, transpose_out=True), what + " cols")
+        elif kind == "mx":
+            q, s = fp8mm.fp8_quantize_mx(xd)
+            rq, rs = mx.quantize_mx(x)
+            assert np.array_equal(host(q), rq) and np.array_equal(host(s), rs), what
+        else:
+            E = int(rng.integers(1, 9))
+            sizes = rng.multinomial(max(rows - int(rng.integers(0, 3)), 0), [1.0 / E] * E)
+            offs = np.cumsum(sizes).astype(np.int32)
+            od = torch.from_numpy(offs).cuda()
+            rq, rs, _ = quant.quantize_grouped_128x1(x, offs)
+            nb = rs.shape[0]
+            if kind == "grouped":
+                q_t, s_t = fp8mm.fp8_quantize_grouped_128x1(xd, od)
+            else:
+                q_row, s_row, q_t, s_t = fp8mm.fp8_quantize_grouped_dual(xd, od)
+                M = int(offs[-1])
+                if M:
+                    rq1, rs1 = quant.quantize_blockwise(x[:M], 1, 128)
+                    assert np.array_equal(host(q_row)[:M], rq1), what + " row codes"
+                    assert np.array_equal(host(s_row)[:, :M], rs1), what + " row scales"
+            assert np.array_equal(host(q_t)[:, :128 * nb], rq), what + " runs"
+            assert np.array_equal(host(s_t)[:nb], rs), what + " run scales"
