@@ -225,3 +225,38 @@ def test_product_path_does_not_reference_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("the oracle", ""), f
+
+
+def test_header_is_plain_c_and_the_library_links_from_c(tmp_path):
+    """The boundary is usable from C: the header compiles as C99 with
+    warnings on, and a C program linked against libfp8mm.so makes host-only
+    calls (the recipe table, an argument rejection and its message)."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "fp8mm.h"
+int main(void) {
+  if (!fp8mm_recipe_pair_supported(FP8MM_BLOCK_1x128, FP8MM_BLOCK_128x128, FP8MM_B_NK)) return 1;
+  if (fp8mm_recipe_pair_supported(FP8MM_ROWWISE, FP8MM_TENSORWISE, FP8MM_B_NK)) return 2;
+  fp8mm_status st = fp8_scaled_mm(0, 64, 256, 256, 0, 64, 256, FP8MM_B_NK, 0, FP8MM_TENSORWISE, 0,
+                                  FP8MM_TENSORWISE, 0, FP8MM_OUT_BF16, 0, 64, 0);
+  if (st != FP8MM_EINVAL || strlen(fp8mm_last_error()) == 0) return 3;
+  if (fp8mm_grouped_runs_capacity(16384, 64) != 192) return 4;
+  printf("ok\n");
+  return 0;
+}
+''')
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{os.path.join(ROOT, 'include')}",
+           "-I/opt/rocm/include", str(src), f"-L{libdir}", "-lfp8mm", f"-Wl,-rpath,{libdir}", "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0 and run.stdout.strip() == "ok", (run.returncode, run.stdout, run.stderr)
