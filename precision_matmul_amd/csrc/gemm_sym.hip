@@ -170,7 +170,8 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     if (g >= tiles_m) return;
     int e = 0;
     int64_t rend = 0;
-    if (!grouped_mtile(p, SY_BM, g, e, row0, rend)) return;
+    // m-tiles with more than 128 rows first, the short ones last (grouped.hpp)
+    if (!grp::find_mtile_long_first(p.offsets, p.E, p.M, g, e, row0, rend)) return;
     rows_valid = int(min<int64_t>(SY_BM, rend - row0));
     Bg = p.B + int64_t(e) * p.N * p.K;
     sbg = p.sb + int64_t(e) * (EPI == Epi::Block128x128 ? (p.N / 128) * (p.K / 128) : p.N);

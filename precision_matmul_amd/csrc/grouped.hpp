@@ -59,6 +59,72 @@ __device__ inline bool find_run(const int32_t* offs, int64_t E, int64_t rows, in
   return false;
 }
 
+// The m-tiles of the grouped GEMM (256 rows) in a load-balancing order: the
+// experts' tiles with more than 128 rows come first (expert order), then
+// their tiles with at most 128 rows (an expert's last tile when its row count
+// leaves a remainder of at most 128), so that the short tiles fill the end of
+// the launch.  Tile g -> expert, first row, end row of the expert; false past
+// the last tile.
+__device__ inline bool find_mtile_long_first(const int32_t* offs, int64_t E, int64_t rows, int g, int& e_out,
+                                             int64_t& row0, int64_t& row_end) {
+  constexpr int BM = 256;
+  const int lane = threadIdx.x & 63;
+  // long tiles of expert e: the full ones plus a remainder of more than 128 rows
+  auto counts = [&](int64_t start, int64_t end, int& nlong, int& nshort) {
+    const int64_t m = end > start ? end - start : 0;
+    const int64_t rem = m % BM;
+    nlong = int(m / BM) + (rem > BM / 2 ? 1 : 0);
+    nshort = (rem > 0 && rem <= BM / 2) ? 1 : 0;
+  };
+  int total_long = 0;
+  for (int64_t e0 = 0; e0 < E; e0 += 64) {
+    const int64_t e = e0 + lane;
+    int nl = 0, ns = 0;
+    if (e < E) {
+      int64_t start, end;
+      expert_range(offs, rows, e, start, end);
+      counts(start, end, nl, ns);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) nl += __shfl_xor(nl, off, 64);
+    total_long += nl;
+  }
+  const bool want_long = g < total_long;
+  const int gg = want_long ? g : g - total_long;
+  int base = 0;
+  for (int64_t e0 = 0; e0 < E; e0 += 64) {
+    const int64_t e = e0 + lane;
+    int64_t start = 0, end = 0;
+    int nl = 0, ns = 0;
+    if (e < E) {
+      expert_range(offs, rows, e, start, end);
+      counts(start, end, nl, ns);
+    }
+    const int cnt = want_long ? nl : ns;
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    const bool hit = (base + incl > gg) && (base + incl - cnt <= gg) && cnt > 0;
+    const unsigned long long mask = __ballot(hit);
+    if (mask) {
+      const int src = __builtin_ctzll(mask);
+      const int excl = __shfl(incl - cnt, src, 64);
+      e_out = int(e0) + src;
+      const int64_t s = __shfl(start, src, 64);
+      const int64_t en = __shfl(end, src, 64);
+      // a long tile j starts at 256 j; the short tile after the full ones
+      row0 = want_long ? s + int64_t(gg - base - excl) * BM : s + (en - s) / BM * BM;
+      row_end = en;
+      return true;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  return false;
+}
+
 // Runs of bm rows of the experts before e (first) and of expert e (count).
 __device__ inline void runs_before(const int32_t* offs, int64_t rows, int bm, int64_t e, int64_t& first,
                                    int& count) {
