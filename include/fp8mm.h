@@ -206,7 +206,8 @@ fp8mm_status fp8_scaled_mm(const uint8_t* A, int64_t M, int64_t K, int64_t lda,
  * group, so no access leaves the arrays; the next expert then starts at the
  * smaller offset, and rows that two experts cover are written twice (their
  * values are undefined).
- * K % 16 == 0. */
+ * K % 16 == 0.  E <= 2^16 here and in every other grouped call (each
+ * workgroup scans the offsets to find its expert). */
 fp8mm_status fp8_scaled_grouped_mm(const uint8_t* A, int64_t M_total,
                                    int64_t K, const uint8_t* B_EnK, int64_t E,
                                    int64_t N, const int32_t* offsets,

@@ -44,6 +44,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // an operand below 2^31 bytes, and a scale array below 2^32 bytes.
 constexpr int64_t kMaxLd = int64_t(1) << 22;
 constexpr int64_t kMaxScales = int64_t(1) << 30;
+// Every workgroup of a grouped kernel scans the E offsets to find its expert,
+// and the grouped grids grow with E: cap E so that a call stays a bounded
+// amount of work.
+constexpr int64_t kMaxExperts = int64_t(1) << 16;
 
 struct PairRule {
   fp8mm_recipe a;
@@ -245,8 +249,8 @@ fp8mm_status fp8_scaled_grouped_mm(const uint8_t* A, int64_t M_total, int64_t K,
   if (!offsets) return fail(FP8MM_EINVAL, "offsets are required for the grouped GEMM");
   if (out_dtype != FP8MM_OUT_BF16 && out_dtype != FP8MM_OUT_FP32) return fail(FP8MM_EINVAL, "unknown out_dtype");
   if (M_total < 0 || K < 0 || N < 0 || E < 0) return fail(FP8MM_EINVAL, "negative shape");
-  if (M_total > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1 || E > (int64_t(1) << 20))
-    return fail(FP8MM_EINVAL, "M_total and N must be < 2^31 and E <= 2^20");
+  if (M_total > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1 || E > kMaxExperts)
+    return fail(FP8MM_EINVAL, "M_total and N must be < 2^31 and E <= 2^16");
   if (K % 16 != 0 || K > kMaxLd) return fail(FP8MM_EINVAL, "K (%lld) must be a multiple of 16 and <= 2^22", (long long)K);
   if (ldo < N) return fail(FP8MM_EINVAL, "ldo (%lld) must be >= N (%lld)", (long long)ldo, (long long)N);
   if (M_total == 0 || N == 0 || E == 0) return ok();
@@ -286,8 +290,8 @@ fp8mm_status fp8_scaled_grouped_mm_v2(const uint8_t* A, int64_t M_total, int64_t
   if (!offsets) return fail(FP8MM_EINVAL, "offsets are required for the grouped GEMM");
   if (out_dtype != FP8MM_OUT_BF16 && out_dtype != FP8MM_OUT_FP32) return fail(FP8MM_EINVAL, "unknown out_dtype");
   if (M_total < 0 || K < 0 || N < 0 || E < 0) return fail(FP8MM_EINVAL, "negative shape");
-  if (M_total > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1 || E > (int64_t(1) << 20))
-    return fail(FP8MM_EINVAL, "M_total and N must be < 2^31 and E <= 2^20");
+  if (M_total > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1 || E > kMaxExperts)
+    return fail(FP8MM_EINVAL, "M_total and N must be < 2^31 and E <= 2^16");
   fp8mm::Epi epi;
   if (recipe_a == FP8MM_ROWWISE && recipe_b == FP8MM_ROWWISE)
     epi = fp8mm::Epi::Row;
@@ -343,7 +347,7 @@ fp8mm_status fp8_quantize_grouped_128x1(const void* x, int64_t T, int64_t C, int
                                         int64_t E, uint8_t* q_t, int64_t ld_q, float* scale, hipStream_t stream) {
   fp8mm_status st = check_quant_common(x, T, C, ld_x, q_t, scale);
   if (st != FP8MM_OK) return st;
-  if (E < 0 || E > (int64_t(1) << 20)) return fail(FP8MM_EINVAL, "E (%lld) must be in [0, 2^20]", (long long)E);
+  if (E < 0 || E > kMaxExperts) return fail(FP8MM_EINVAL, "E (%lld) must be in [0, 2^16]", (long long)E);
   if (!offsets && E > 0) return fail(FP8MM_EINVAL, "offsets are required");
   const int64_t runs = T / 128 + E;
   if (ld_q < 128 * runs || ld_q % 16 != 0 || ld_q > kMaxLd)
@@ -362,7 +366,7 @@ fp8mm_status fp8_quantize_grouped_dual(const void* x, int64_t T, int64_t C, int6
                                        int64_t ld_q, float* scale_t, hipStream_t stream) {
   fp8mm_status st = check_quant_common(x, T, C, ld_x, q_t, scale_t);
   if (st != FP8MM_OK) return st;
-  if (E < 0 || E > (int64_t(1) << 20)) return fail(FP8MM_EINVAL, "E (%lld) must be in [0, 2^20]", (long long)E);
+  if (E < 0 || E > kMaxExperts) return fail(FP8MM_EINVAL, "E (%lld) must be in [0, 2^16]", (long long)E);
   if (!offsets && E > 0) return fail(FP8MM_EINVAL, "offsets are required");
   if (C % 128 != 0) return fail(FP8MM_EINVAL, "C (%lld) must be a multiple of 128", (long long)C);
   const int64_t runs = T / 128 + E;
@@ -387,8 +391,8 @@ fp8mm_status fp8_grouped_linear_grad_weight(const uint8_t* gt_q, int64_t N_out, 
                                             void* grad_w, hipStream_t stream) {
   if (out_dtype != FP8MM_OUT_BF16 && out_dtype != FP8MM_OUT_FP32) return fail(FP8MM_EINVAL, "unknown out_dtype");
   if (N_out < 0 || K_in < 0 || T < 0 || E < 0) return fail(FP8MM_EINVAL, "negative shape");
-  if (N_out > (int64_t(1) << 31) - 1 || K_in > (int64_t(1) << 31) - 1 || E > (int64_t(1) << 20))
-    return fail(FP8MM_EINVAL, "N_out and K_in must be < 2^31 and E <= 2^20");
+  if (N_out > (int64_t(1) << 31) - 1 || K_in > (int64_t(1) << 31) - 1 || E > kMaxExperts)
+    return fail(FP8MM_EINVAL, "N_out and K_in must be < 2^31 and E <= 2^16");
   if (!offsets && E > 0) return fail(FP8MM_EINVAL, "offsets are required");
   const int64_t runs = T / 128 + E;
   if (ld < 128 * runs || ld % 16 != 0 || ld > kMaxLd)

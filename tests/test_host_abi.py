@@ -130,6 +130,8 @@ def test_grouped_v2_checks_recipes_and_shapes(lib):
     assert call(ldo=64) == _lib.EINVAL
     assert call(A=FAKE + 8) == _lib.EINVAL
     assert call(E=-1) == _lib.EINVAL
+    assert call(E=(1 << 16) + 1) == _lib.EINVAL                # expert count cap
+    assert "E <= 2^16" in lib.fp8mm_last_error().decode()
     assert call(M=0) == _lib.OK                                # empty: nothing to do
 
 
@@ -146,6 +148,8 @@ def test_grouped_weight_gradient_entries_check_capacity(lib):
     assert q(FAKE, 1000, 64, 64, FAKE, 8, FAKE, cap + 8, FAKE, None) == _lib.EINVAL     # ld_q % 16
     assert q(FAKE, 1000, 64, 64, FAKE, 8, FAKE, cap, None, None) == _lib.EINVAL         # scale NULL
     assert q(FAKE, 1000, 64, 64, FAKE, -1, FAKE, cap, FAKE, None) == _lib.EINVAL
+    assert q(FAKE, 1000, 64, 64, FAKE, (1 << 16) + 1, FAKE, cap, FAKE, None) == _lib.EINVAL
+    assert "2^16" in lib.fp8mm_last_error().decode()
     g = lib.fp8_grouped_linear_grad_weight
     # gt_q, N_out, gt_scale, xt_q, K_in, xt_scale, ld, T, offsets, E, od, grad_w, stream
     assert g(FAKE, 64, FAKE, FAKE, 64, FAKE, cap - 128, 1000, FAKE, 8, 0, FAKE, None) == _lib.EINVAL
@@ -154,6 +158,8 @@ def test_grouped_weight_gradient_entries_check_capacity(lib):
     assert g(FAKE + 4, 64, FAKE, FAKE, 64, FAKE, cap, 1000, FAKE, 8, 0, FAKE, None) == _lib.EINVAL
     assert g(FAKE, 64, None, FAKE, 64, FAKE, cap, 1000, FAKE, 8, 0, FAKE, None) == _lib.EINVAL
     assert g(FAKE, 0, FAKE, FAKE, 64, FAKE, cap, 1000, FAKE, 8, 0, FAKE, None) == _lib.OK
+    assert g(FAKE, 64, FAKE, FAKE, 64, FAKE, cap, 1000, FAKE, (1 << 16) + 1, 0, FAKE, None) == _lib.EINVAL
+    assert "E <= 2^16" in lib.fp8mm_last_error().decode()
     big = 1 << 22                                                 # ld / 128 = 32768 runs
     assert g(FAKE, 1 << 16, FAKE, FAKE, 64, FAKE, big, 1000, FAKE, 8, 0, FAKE, None) == _lib.EINVAL   # scales
 
@@ -168,6 +174,7 @@ def test_grouped_dual_quantizer_rejects_before_launch(lib):
     assert d(FAKE, 1000, 128, 128, FAKE, 8, FAKE + 8, 128, FAKE, FAKE, cap, FAKE, None) == _lib.EINVAL
     assert d(FAKE, 1000, 128, 128, FAKE, 8, FAKE, 128, FAKE, FAKE, cap - 128, FAKE, None) == _lib.EINVAL
     assert d(FAKE, 1000, 128, 128, None, 8, FAKE, 128, FAKE, FAKE, cap, FAKE, None) == _lib.EINVAL   # offsets
+    assert d(FAKE, 1000, 128, 128, FAKE, (1 << 16) + 1, FAKE, 128, FAKE, FAKE, cap, FAKE, None) == _lib.EINVAL
 
 
 def test_quantizers_reject_before_launch(lib):
