@@ -195,8 +195,8 @@ def fp8_scaled_mm(A, B, scale_a, recipe_a, scale_b, recipe_b, b_layout="NK", bia
             raise ValueError("bias must be a contiguous bf16 tensor of N elements")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=A.device)
-    elif out.dtype != out_dtype or tuple(out.shape) != (M, N):
-        raise ValueError("out has the wrong dtype or shape")
+    elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or out.device != A.device:
+        raise ValueError("out has the wrong dtype, shape or device")
     st = _lib.load().fp8_scaled_mm(A.data_ptr(), M, K, _ld(A, "A"), B.data_ptr(), N, _ld(B, "B"),
                                    _lib.B_LAYOUTS[b_layout], scale_a.data_ptr(), _recipe(recipe_a),
                                    scale_b.data_ptr(), _recipe(recipe_b), _ptr(bias), _out_code(out_dtype),
@@ -234,6 +234,8 @@ def fp8_scaled_grouped_mm(A, B_EnK, offsets, scale_a, scale_b, bias=None, out_dt
             raise ValueError("bias must be a contiguous bf16 [E, N] tensor")
     if out is None:
         out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or out.device != A.device:
+        raise ValueError("out has the wrong dtype, shape or device")
     st = _lib.load().fp8_scaled_grouped_mm(A.data_ptr(), M, K, B_EnK.data_ptr(), E, N, offsets.data_ptr(),
                                            scale_a.data_ptr(), scale_b.data_ptr(), _ptr(bias),
                                            _out_code(out_dtype), out.data_ptr(), _ld(out, "out"), _stream(A))
@@ -285,6 +287,8 @@ def fp8_scaled_grouped_mm_v2(A, B_E, offsets, scale_a, recipe_a, scale_b, recipe
             raise ValueError("bias must be a contiguous bf16 [E, N] tensor")
     if out is None:
         out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or out.device != A.device:
+        raise ValueError("out has the wrong dtype, shape or device")
     st = _lib.load().fp8_scaled_grouped_mm_v2(A.data_ptr(), M, K, B_E.data_ptr(), E, N, _lib.B_LAYOUTS[b_layout],
                                               offsets.data_ptr(), scale_a.data_ptr(), ra, scale_b.data_ptr(), rb,
                                               _ptr(bias), _out_code(out_dtype), out.data_ptr(), _ld(out, "out"),

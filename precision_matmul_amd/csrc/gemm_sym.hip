@@ -112,14 +112,14 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---------------- tile ----------------
-  // Grouped (MoE) problems: m-tiles g of all experts (expert order) go to the
-  // 8 XCDs (workgroups are dealt to them round-robin, XCD = b % 8) in chunks
-  // of SY_GCH consecutive m-tiles, chunk c to XCD c % 8; an XCD walks its
-  // m-tiles in order, all n-tiles tn of one m-tile together.  So the n-tiles
-  // of one m-tile share its A rows in one XCD's L2, the m-tiles of one expert
-  // (consecutive g) mostly share its B tiles there too, and the real m-tiles
-  // (a prefix of the upper bound the grid is sized for) are spread over all
-  // XCDs.
+  // Grouped (MoE) problems: m-tiles g of all experts (in the order chosen
+  // below) go to the 8 XCDs (workgroups are dealt to them round-robin, XCD =
+  // b % 8) in chunks of SY_GCH consecutive m-tiles, chunk c to XCD c % 8; an
+  // XCD walks its m-tiles in order, all n-tiles tn of one m-tile together.
+  // So the n-tiles of one m-tile share its A rows in one XCD's L2, the
+  // m-tiles of one expert (consecutive g) mostly share its B tiles there too,
+  // and the real m-tiles (a prefix of the upper bound the grid is sized for)
+  // are spread over all XCDs.
   // Expert e's B is [N, K] (or [K, N]) at B + e N K, its bias row e of
   // [E, N], its scales row e of [E, N] (rowwise) or grid e of [E, N/128 x
   // K/128] (128x128).
@@ -170,8 +170,16 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     if (g >= tiles_m) return;
     int e = 0;
     int64_t rend = 0;
-    // m-tiles with more than 128 rows first, the short ones last (grouped.hpp)
-    if (!grp::find_mtile_long_first(p.offsets, p.E, p.M, g, e, row0, rend)) return;
+    // B stored [N, K]: m-tiles with more than 128 rows first, the short ones
+    // last (grouped.hpp).  B stored [K, N]: expert order, so an expert's
+    // short last m-tile runs beside its full ones and finds their B tiles
+    // in L2 (measured 7 % faster there; the [N, K] form gains from the order
+    // instead).
+    if constexpr (B_KN) {
+      if (!grp::find_run(p.offsets, p.E, p.M, SY_BM, g, e, row0, rend)) return;
+    } else {
+      if (!grp::find_mtile_long_first(p.offsets, p.E, p.M, g, e, row0, rend)) return;
+    }
     rows_valid = int(min<int64_t>(SY_BM, rend - row0));
     Bg = p.B + int64_t(e) * p.N * p.K;
     sbg = p.sb + int64_t(e) * (EPI == Epi::Block128x128 ? (p.N / 128) * (p.K / 128) : p.N);
@@ -501,6 +509,102 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     }
   };
 
+  // Grouped short tile (at most 64 rows): K loop and stores, entered with
+  // stage 0 complete and visible.
+  [[maybe_unused]] auto short_tile = [&]() {
+    const int cb = wave * 32;                       // the wave's first column in the tile
+    const bool cact = cb < cols_valid;              // wave-uniform
+    v4f sacc[SY_FM][2];
+#pragma unroll
+    for (int i = 0; i < SY_FM; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sacc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    load_group(false, 1, lds1);
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint32_t this_st = (kt & 1) ? lds1 : lds0;
+      const uint32_t next_st = (kt & 1) ? lds0 : lds1;
+      const uint8_t* St = (kt & 1) ? stage1 : stage0;
+      load_group(true, kt + 1, next_st);
+      if constexpr (BLOCKWISE) load_scales(kt + 1, next_st);
+      if (cact) {
+        v8i fa_s[SY_FM], fb_s[2];
+#pragma unroll
+        for (int i = 0; i < SY_FM; ++i) fa_s[i] = read_frag(St, i * 16 + frow);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb_s[j] = read_b(St + SY_A, cb + j * 16);
+        if constexpr (BLOCKWISE) {
+          // 1x128 x 128x128: the step's partial times sA(row) sB(block)
+          const float* sas = reinterpret_cast<const float*>(St + SY_A + SY_B);
+          const float sbk = sas[SY_SCALE / 4 + (cb / 128) * 64];
+#pragma unroll
+          for (int i = 0; i < SY_FM; ++i) {
+            const float f = sas[i * 16 + frow] * sbk;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const v4f t = mfma_16x16x128(fb_s[j], fa_s[i], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sacc[i][j][e] = __builtin_fmaf(t[e], f, sacc[i][j][e]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < SY_FM; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) sacc[i][j] = mfma_16x16x128(fb_s[j], fa_s[i], sacc[i][j]);
+        }
+      }
+      // every wave has read this stage and its loads of the next have landed
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      sy_fence();
+      asm volatile("s_barrier" ::: "memory");
+      sy_fence();
+      load_group(false, kt + 2, this_st);
+    }
+    if (!cact) return;
+    // stores: 4 adjacent columns per lane and fragment, one 8- or 16-byte
+    // non-temporal store where they are all inside the tile
+#pragma unroll
+    for (int i = 0; i < SY_FM; ++i) {
+      const int r = i * 16 + frow;
+      if (r >= rows_valid) continue;
+      [[maybe_unused]] float sr = 1.f;
+      if constexpr (EPI == Epi::Row) sr = p.sa[row0 + r];
+      uint8_t* orow = reinterpret_cast<uint8_t*>(p.out) + (out_off + (row0 + r) * p.ldo + n0) * OUTB;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = cb + j * 16 + fq * 4;
+        if (c >= cols_valid) continue;
+        const int n = min(4, cols_valid - c);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = sacc[i][j][e];
+          if (e < n) {
+            if constexpr (EPI == Epi::Row) v[e] = (v[e] * sr) * sbg[n0 + c + e];
+            if constexpr (BIAS) v[e] = v[e] + __uint_as_float(uint32_t(biasg[n0 + c + e]) << 16);
+          }
+        }
+        uint8_t* dst = orow + c * OUTB;
+        if (vec_out && n == 4) {
+          if constexpr (OUT_BF16) {
+            const v2i w{int(uint32_t(f32_to_bf16_rne(v[0])) | (uint32_t(f32_to_bf16_rne(v[1])) << 16)),
+                        int(uint32_t(f32_to_bf16_rne(v[2])) | (uint32_t(f32_to_bf16_rne(v[3])) << 16))};
+            __builtin_nontemporal_store(w, reinterpret_cast<v2i*>(dst));
+          } else {
+            __builtin_nontemporal_store(v4f{v[0], v[1], v[2], v[3]}, reinterpret_cast<v4f*>(dst));
+          }
+        } else {
+          for (int e = 0; e < n; ++e) {
+            if constexpr (OUT_BF16)
+              reinterpret_cast<uint16_t*>(dst)[e] = f32_to_bf16_rne(v[e]);
+            else
+              reinterpret_cast<float*>(dst)[e] = v[e];
+          }
+        }
+      }
+    }
+  };
+
   if (nk > 0) {
     // Prologue: stage 0 complete and visible; the fragments and factors of
     // step 0 in registers; the first loads of step 1 in flight.
@@ -509,6 +613,18 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     if constexpr (BLOCKWISE || MX) load_scales(0, lds0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if constexpr (GROUPED) {
+      // An expert's last m-tile with at most 64 rows (the remainder past its
+      // full tiles).  In the layout above only two waves, on two SIMDs, would
+      // have rows to compute; here all 8 do: wave w takes the 64 x 32 block
+      // at columns [32 w, 32 w + 32), in the transposed operand order (lane:
+      // row 16 i + frow, columns 16 j + 4 fq + e).  Loads, stages and the
+      // one barrier per K step are those of the full tile.
+      if (__builtin_amdgcn_readfirstlane(rows_valid) <= SY_TM) {
+        short_tile();
+        return;
+      }
+    }
     if (active) {
 #pragma unroll
       for (int i = 0; i < SY_FM; ++i) a[i] = read_frag(stage0, row_base + i * 16 + frow);

@@ -101,6 +101,56 @@ def test_grouped_rowwise_weights_stored_kn(N):
     _assert_close(out_f64(out)[written], ref[written], f"grouped rowwise KN N={N}")
 
 
+@pytest.mark.parametrize("N,ld_pad,out_dtype", [(406, 0, torch.bfloat16), (406, 10, torch.bfloat16),
+                                                  (406, 2, torch.float32), (512, 0, torch.float32)])
+def test_grouped_rowwise_short_remainders(N, ld_pad, out_dtype):
+    """Experts whose last m-tile holds 1 to 64 rows (the short-tile path: all
+    waves on a 64 x 256 block), next to full and 65-row tiles; N = 406 ends
+    the last 256-column tile after 150 columns (a lane's group of four partly
+    outside it); out with ld = N or padded (16-byte vector stores where the
+    padding aligns every row); bias per expert."""
+    E, K = 9, 384
+    sizes = np.array([256 + 1, 64, 0, 256 + 63, 65, 17, 256, 256 + 40, 3])
+    g = workloads.streams(N + ld_pad, 3)
+    M = int(sizes.sum())
+    act = workloads.normal_bf16(g[0], (M + 4, K))                 # 4 trailing rows no expert owns
+    W = workloads.normal_bf16(g[1], (E * N, K), 0.02)
+    bias = workloads.normal_bf16(g[2], (E, N), 0.5)
+    offs = np.cumsum(sizes).astype(np.int32)
+    qa, sa = fp8mm.fp8_quantize_rowwise(bf16_dev(act))
+    ra, rsa = quant.quantize_rowwise(act)
+    qw, sw = fp8mm.fp8_quantize_rowwise(bf16_dev(W))
+    rw, rsw = quant.quantize_rowwise(W)
+    full = torch.zeros((M + 4, N + ld_pad), dtype=out_dtype, device="cuda")
+    out = full[:, :N]
+    say(f"grouped rowwise short remainders N={N} ld={N + ld_pad} {out_dtype}")
+    fp8mm.fp8_scaled_grouped_mm(qa, qw.reshape(E, N, K), _offs_dev(offs), sa.reshape(-1), sw.reshape(E, N),
+                                bias=bf16_dev(bias), out_dtype=out_dtype, out=out)
+    ref, written = gemm.grouped_mm(ra, rw.reshape(E, N, K), offs, rsa, rsw.reshape(E, N),
+                                   bias=quant.bf16_to_f32(bias), out_dtype=None)
+    got = out_f64(full)
+    assert np.all(got[:, N:] == 0), "columns past N must not be written"
+    assert np.all(got[:, :N][~written] == 0), "rows no expert owns must not be written"
+    _assert_close(got[:, :N][written], ref[written], f"grouped rowwise short N={N}",
+                  out_dtype="fp32" if out_dtype == torch.float32 else "bf16")
+
+
+def test_grouped_out_argument_is_checked():
+    E, N, K = 2, 128, 128
+    qa = torch.zeros((10, K), dtype=torch.uint8, device="cuda")
+    qw = torch.zeros((E, N, K), dtype=torch.uint8, device="cuda")
+    sa = torch.ones(10, device="cuda")
+    sw = torch.ones(E * N, device="cuda")
+    offs = _offs_dev([4, 10])
+    for out in (torch.zeros((10, N), dtype=torch.bfloat16, device="cuda"),     # dtype: fp32 asked
+                torch.zeros((9, N), dtype=torch.float32, device="cuda")):       # shape
+        with pytest.raises(ValueError):
+            fp8mm.fp8_scaled_grouped_mm(qa, qw, offs, sa, sw.reshape(E, N), out_dtype=torch.float32, out=out)
+        with pytest.raises(ValueError):
+            fp8mm.fp8_scaled_grouped_mm_v2(qa, qw, offs, sa, "rowwise", sw, "rowwise", out_dtype=torch.float32,
+                                           out=out)
+
+
 def test_grouped_v2_rowwise_matches_v1():
     E, N, K = 6, 256, 384
     sizes = np.array([10, 200, 0, 31, 128, 77])
