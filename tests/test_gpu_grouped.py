@@ -101,17 +101,19 @@ def test_grouped_rowwise_weights_stored_kn(N):
     _assert_close(out_f64(out)[written], ref[written], f"grouped rowwise KN N={N}")
 
 
-@pytest.mark.parametrize("N,ld_pad,out_dtype", [(406, 0, torch.bfloat16), (406, 10, torch.bfloat16),
-                                                  (406, 2, torch.float32), (512, 0, torch.float32)])
-def test_grouped_rowwise_short_remainders(N, ld_pad, out_dtype):
+@pytest.mark.parametrize("N,ld_pad,out_dtype,K", [(406, 0, torch.bfloat16, 384), (406, 10, torch.bfloat16, 384),
+                                                    (406, 2, torch.float32, 384), (512, 0, torch.float32, 384),
+                                                    (406, 10, torch.bfloat16, 400)])
+def test_grouped_rowwise_short_remainders(N, ld_pad, out_dtype, K):
     """Experts whose last m-tile holds 1 to 64 rows (the short-tile path: all
     waves on a 64 x 256 block), next to full and 65-row tiles; N = 406 ends
     the last 256-column tile after 150 columns (a lane's group of four partly
     outside it); out with ld = N or padded (16-byte vector stores where the
-    padding aligns every row); bias per expert."""
-    E, K = 9, 384
+    padding aligns every row); bias per expert; K = 400 ends the last K step
+    after 16 of its 128 bytes."""
+    E = 9
     sizes = np.array([256 + 1, 64, 0, 256 + 63, 65, 17, 256, 256 + 40, 3])
-    g = workloads.streams(N + ld_pad, 3)
+    g = workloads.streams(N + ld_pad + K, 3)
     M = int(sizes.sum())
     act = workloads.normal_bf16(g[0], (M + 4, K))                 # 4 trailing rows no expert owns
     W = workloads.normal_bf16(g[1], (E * N, K), 0.02)
@@ -123,7 +125,7 @@ def test_grouped_rowwise_short_remainders(N, ld_pad, out_dtype):
     rw, rsw = quant.quantize_rowwise(W)
     full = torch.zeros((M + 4, N + ld_pad), dtype=out_dtype, device="cuda")
     out = full[:, :N]
-    say(f"grouped rowwise short remainders N={N} ld={N + ld_pad} {out_dtype}")
+    say(f"grouped rowwise short remainders N={N} K={K} ld={N + ld_pad} {out_dtype}")
     fp8mm.fp8_scaled_grouped_mm(qa, qw.reshape(E, N, K), _offs_dev(offs), sa.reshape(-1), sw.reshape(E, N),
                                 bias=bf16_dev(bias), out_dtype=out_dtype, out=out)
     ref, written = gemm.grouped_mm(ra, rw.reshape(E, N, K), offs, rsa, rsw.reshape(E, N),
