@@ -509,16 +509,21 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     }
   };
 
-  // Grouped short tile (at most 64 rows): K loop and stores, entered with
-  // stage 0 complete and visible.
-  [[maybe_unused]] auto short_tile = [&]() {
-    const int cb = wave * 32;                       // the wave's first column in the tile
-    const bool cact = cb < cols_valid;              // wave-uniform
-    v4f sacc[SY_FM][2];
+  // Grouped short tile: K loop and stores, entered with stage 0 complete and
+  // visible.  FNS = 2 (at most 64 rows): wave w takes the 64 x 32 block at
+  // rows [0, 64), columns [32 w, 32 w + 32).  FNS = 4 (at most 128 rows):
+  // the 64 x 64 block at rows [64 (w & 1), +64), columns [64 (w >> 1), +64),
+  // so the two waves of a SIMD (w, w + 4) share rows but not columns.
+  [[maybe_unused]] auto short_tile = [&](auto fns_c) {
+    constexpr int FNS = decltype(fns_c)::value;
+    const int rb = FNS == 2 ? 0 : (wave & 1) * 64;           // the wave's first row in the tile
+    const int cb = FNS == 2 ? wave * 32 : (wave >> 1) * 64;  // its first column
+    const bool cact = rb < rows_valid && cb < cols_valid;    // wave-uniform
+    v4f sacc[SY_FM][FNS];
 #pragma unroll
     for (int i = 0; i < SY_FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) sacc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < FNS; ++j) sacc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     load_group(false, 1, lds1);
     for (int kt = 0; kt < nk; ++kt) {
       const uint32_t this_st = (kt & 1) ? lds1 : lds0;
@@ -527,20 +532,20 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       load_group(true, kt + 1, next_st);
       if constexpr (BLOCKWISE) load_scales(kt + 1, next_st);
       if (cact) {
-        v8i fa_s[SY_FM], fb_s[2];
+        v8i fa_s[SY_FM], fb_s[FNS];
 #pragma unroll
-        for (int i = 0; i < SY_FM; ++i) fa_s[i] = read_frag(St, i * 16 + frow);
+        for (int i = 0; i < SY_FM; ++i) fa_s[i] = read_frag(St, rb + i * 16 + frow);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb_s[j] = read_b(St + SY_A, cb + j * 16);
+        for (int j = 0; j < FNS; ++j) fb_s[j] = read_b(St + SY_A, cb + j * 16);
         if constexpr (BLOCKWISE) {
           // 1x128 x 128x128: the step's partial times sA(row) sB(block)
           const float* sas = reinterpret_cast<const float*>(St + SY_A + SY_B);
           const float sbk = sas[SY_SCALE / 4 + (cb / 128) * 64];
 #pragma unroll
           for (int i = 0; i < SY_FM; ++i) {
-            const float f = sas[i * 16 + frow] * sbk;
+            const float f = sas[rb + i * 16 + frow] * sbk;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < FNS; ++j) {
               const v4f t = mfma_16x16x128(fb_s[j], fa_s[i], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
               for (int e = 0; e < 4; ++e) sacc[i][j][e] = __builtin_fmaf(t[e], f, sacc[i][j][e]);
@@ -550,7 +555,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
 #pragma unroll
           for (int i = 0; i < SY_FM; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) sacc[i][j] = mfma_16x16x128(fb_s[j], fa_s[i], sacc[i][j]);
+            for (int j = 0; j < FNS; ++j) sacc[i][j] = mfma_16x16x128(fb_s[j], fa_s[i], sacc[i][j]);
         }
       }
       // every wave has read this stage and its loads of the next have landed
@@ -565,13 +570,13 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     // non-temporal store where they are all inside the tile
 #pragma unroll
     for (int i = 0; i < SY_FM; ++i) {
-      const int r = i * 16 + frow;
+      const int r = rb + i * 16 + frow;
       if (r >= rows_valid) continue;
       [[maybe_unused]] float sr = 1.f;
       if constexpr (EPI == Epi::Row) sr = p.sa[row0 + r];
       uint8_t* orow = reinterpret_cast<uint8_t*>(p.out) + (out_off + (row0 + r) * p.ldo + n0) * OUTB;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < FNS; ++j) {
         const int c = cb + j * 16 + fq * 4;
         if (c >= cols_valid) continue;
         const int n = min(4, cols_valid - c);
@@ -614,14 +619,19 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if constexpr (GROUPED) {
-      // An expert's last m-tile with at most 64 rows (the remainder past its
-      // full tiles).  In the layout above only two waves, on two SIMDs, would
-      // have rows to compute; here all 8 do: wave w takes the 64 x 32 block
-      // at columns [32 w, 32 w + 32), in the transposed operand order (lane:
-      // row 16 i + frow, columns 16 j + 4 fq + e).  Loads, stages and the
-      // one barrier per K step are those of the full tile.
-      if (__builtin_amdgcn_readfirstlane(rows_valid) <= SY_TM) {
-        short_tile();
+      // An expert's last m-tile with at most 128 rows (the remainder past its
+      // full tiles).  In the layout above at most four waves would have rows
+      // to compute, two of them on one SIMD; here all 8 do, in the
+      // transposed operand order (lane: row 16 i + frow, columns 16 j + 4 fq
+      // + e).  Loads, stages and the one barrier per K step are those of the
+      // full tile.
+      const int rv = __builtin_amdgcn_readfirstlane(rows_valid);
+      if (rv <= SY_TM) {
+        short_tile(std::integral_constant<int, 2>{});
+        return;
+      }
+      if (rv <= 2 * SY_TM) {
+        short_tile(std::integral_constant<int, 4>{});
         return;
       }
     }

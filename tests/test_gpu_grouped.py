@@ -105,14 +105,15 @@ def test_grouped_rowwise_weights_stored_kn(N):
                                                     (406, 2, torch.float32, 384), (512, 0, torch.float32, 384),
                                                     (406, 10, torch.bfloat16, 400)])
 def test_grouped_rowwise_short_remainders(N, ld_pad, out_dtype, K):
-    """Experts whose last m-tile holds 1 to 64 rows (the short-tile path: all
-    waves on a 64 x 256 block), next to full and 65-row tiles; N = 406 ends
+    """Experts whose last m-tile holds 1 to 64 rows or 65 to 128 rows (the
+    two short-tile layouts: all waves on a 64 x 256 or 128 x 256 block), next
+    to full tiles; N = 406 ends
     the last 256-column tile after 150 columns (a lane's group of four partly
     outside it); out with ld = N or padded (16-byte vector stores where the
     padding aligns every row); bias per expert; K = 400 ends the last K step
     after 16 of its 128 bytes."""
-    E = 9
-    sizes = np.array([256 + 1, 64, 0, 256 + 63, 65, 17, 256, 256 + 40, 3])
+    sizes = np.array([256 + 1, 64, 0, 256 + 63, 65, 17, 256, 256 + 40, 3, 256 + 100, 128, 97])
+    E = len(sizes)
     g = workloads.streams(N + ld_pad + K, 3)
     M = int(sizes.sum())
     act = workloads.normal_bf16(g[0], (M + 4, K))                 # 4 trailing rows no expert owns
