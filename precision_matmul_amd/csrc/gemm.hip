@@ -41,6 +41,7 @@
 #include "gemm_common.hpp"
 
 #include <algorithm>
+#include <atomic>
 
 namespace fp8mm {
 namespace {
@@ -627,17 +628,19 @@ hipError_t launch_group_k(const GemmProblem& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-  static int cache[64] = {0};
+// Compute units of the device the stream belongs to, cached per device.
+// Calls from several host threads may fill an entry at once; they store the
+// same value, through atomics.
+static int device_cus(hipStream_t st) {
+  static std::atomic<int> cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  if (hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 // The tail rows of a plain GEMM.  A short tail (its 128 x 128 tiles fit in
@@ -774,7 +777,7 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
   // takes the rows of tiles that fill whole rounds and the rest of the rows
   // (the tail) run with 128 x 128 tiles, four times as many workgroups.
   const int64_t tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
-  const int64_t tiles = tiles_m * tiles_n, cus = device_cus();
+  const int64_t tiles = tiles_m * tiles_n, cus = device_cus(st);
   // Small problems (even 128 x 128 tiles fill at most half the device): four
   // times as many workgroups on 128 x 128 tiles finish sooner.
   if (4 * tiles <= cus / 2) return launch_gemm_tail(p, true, st);
