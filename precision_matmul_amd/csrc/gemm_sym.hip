@@ -36,6 +36,11 @@
 // of step k.  Each wave loads 32 rows of A and 32 of B with one group of
 // four 1 KiB loads (one M0 write per group).
 //
+// Grouped short tiles.  An expert's last m-tile of at most 128 rows keeps
+// the loads, stages and barriers above but spreads its outputs over all 8
+// waves (64 x 32 or 64 x 64 blocks, transposed operand order), since the
+// 64 x 128 sub-tiles would leave most waves without rows.
+//
 // Fragment K order.  Lane l of an MFMA operand supplies 32 bytes that the
 // instruction treats as k in [32 q, 32 q + 32), q = l / 16.  A and B only
 // need the same k order, so each lane supplies the 16-byte chunks q and
