@@ -40,12 +40,14 @@ constexpr float kFastDivMinScale = 8.077935669463161e-28f;  // 2^-90
 // (Markstein's theorem: with a correctly rounded reciprocal one correction
 // gives the correctly rounded quotient).  Valid for s >= 2^-90 and quotients
 // of at least 2^-12 in magnitude; smaller quotients (where a subnormal
-// residual can leave the last bit off) all encode to the same signed zero
-// code.  Checked on the device over the whole input domain of the
-// quantizers: every finite bf16 x with |x| <= amax, against s = fl32(amax /
+// residual can leave the last bit off) all encode to the zero magnitude, and
+// the kernels take the code's sign from x.  tests/host/div_by_scale_check.cpp
+// builds this header for the host and checks it over the whole input domain
+// of the quantizers: every bf16 x with |x| <= amax, against s = fl32(amax /
 // 448) and s = fl32(fl32(amax / 448) + 1e-12) for every positive finite bf16
-// amax with s >= 2^-90 (2 x 2.1e9 pairs): no quotient of magnitude >= 2^-12
-// differs from IEEE division and no e4m3 code differs.
+// amax (2.1e9 pairs): no quotient of magnitude >= 2^-12 differs from IEEE
+// division, every smaller one stays below 2^-10, and the fast path is taken
+// exactly when s >= 2^-90.
 FP8MM_HD float div_by_scale(float x, float s, float r) {
 #pragma clang fp contract(off)
   const float q0 = x * r;
