@@ -197,7 +197,8 @@ fp8mm_status fp8_scaled_mm(const uint8_t* A, int64_t M, int64_t K, int64_t lda,
  *   B_EnK: uint8 [E, N, K] expert weights (K contiguous), scale_b [E, N].
  *   offsets: DEVICE int32 [E], cumulative END row offsets: expert e owns rows
  *     [offsets[e-1], offsets[e]) (offsets[-1] = 0); required (NULL -> EINVAL).
- *   bias: NULL or bf16 [E, N] (per expert).
+ *   bias: NULL or bf16 [N], added to every expert's rows (per-expert bias
+ *     rows: fp8_scaled_grouped_mm_v2 with bias_per_expert = 1).
  *   out: [M_total, N], leading dimension ldo >= N.  Rows at or past
  *     offsets[E-1] are not written.
  * Offsets are read on the device only; they are not validated on the host
@@ -233,8 +234,11 @@ fp8mm_status fp8_scaled_grouped_mm(const uint8_t* A, int64_t M_total,
  *     blockwise recipe applied per expert.
  *   Any other pair -> FP8MM_ENOTIMPL.
  *   B_KN: N % 16 == 0 and K * N < 2^31.
- *   offsets, bias ([E, N] or NULL), out and the treatment of the offsets:
- *   as fp8_scaled_grouped_mm.  K % 16 == 0. */
+ *   bias: NULL, or bf16 [N] shared by every expert (bias_per_expert = 0),
+ *     or bf16 [E, N], row e for expert e (bias_per_expert = 1); any other
+ *     bias_per_expert -> FP8MM_EINVAL.
+ *   offsets, out and the treatment of the offsets: as
+ *   fp8_scaled_grouped_mm.  K % 16 == 0. */
 fp8mm_status fp8_scaled_grouped_mm_v2(const uint8_t* A, int64_t M_total,
                                       int64_t K, const uint8_t* B_E, int64_t E,
                                       int64_t N, fp8mm_b_layout b_layout,
@@ -243,6 +247,7 @@ fp8mm_status fp8_scaled_grouped_mm_v2(const uint8_t* A, int64_t M_total,
                                       fp8mm_recipe recipe_a,
                                       const float* scale_b,
                                       fp8mm_recipe recipe_b, const void* bias,
+                                      int bias_per_expert,
                                       fp8mm_out_dtype out_dtype, void* out,
                                       int64_t ldo, hipStream_t stream);
 

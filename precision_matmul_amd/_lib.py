@@ -28,7 +28,8 @@ SIGNATURES = {
     "fp8_quantize_mx": (_i, [_p, _i64, _i64, _i64, _p, _i64, _p, _p]),
     "fp8_scaled_mm": (_i, [_p, _i64, _i64, _i64, _p, _i64, _i64, _i, _p, _i, _p, _i, _p, _i, _p, _i64, _p]),
     "fp8_scaled_grouped_mm": (_i, [_p, _i64, _i64, _p, _i64, _i64, _p, _p, _p, _p, _i, _p, _i64, _p]),
-    "fp8_scaled_grouped_mm_v2": (_i, [_p, _i64, _i64, _p, _i64, _i64, _i, _p, _p, _i, _p, _i, _p, _i, _p, _i64, _p]),
+    "fp8_scaled_grouped_mm_v2": (_i, [_p, _i64, _i64, _p, _i64, _i64, _i, _p, _p, _i, _p, _i, _p, _i, _i, _p, _i64,
+                                      _p]),
     "fp8mm_grouped_runs_capacity": (_i64, [_i64, _i64]),
     "fp8_quantize_grouped_128x1": (_i, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p]),
     "fp8_quantize_grouped_dual": (_i, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _p]),

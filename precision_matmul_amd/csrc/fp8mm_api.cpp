@@ -270,6 +270,7 @@ fp8mm_status fp8_scaled_grouped_mm(const uint8_t* A, int64_t M_total, int64_t K,
   p.lda = K;
   p.ldb = K;
   p.ldo = ldo;
+  p.bias_stride_e = 0;   // one bf16 [N] bias row for every expert
   p.epi = fp8mm::Epi::Row;
   p.b_kn = false;
   p.out_bf16 = out_dtype == FP8MM_OUT_BF16;
@@ -283,9 +284,10 @@ fp8mm_status fp8_scaled_grouped_mm(const uint8_t* A, int64_t M_total, int64_t K,
 fp8mm_status fp8_scaled_grouped_mm_v2(const uint8_t* A, int64_t M_total, int64_t K, const uint8_t* B_E, int64_t E,
                                       int64_t N, fp8mm_b_layout b_layout, const int32_t* offsets,
                                       const float* scale_a, fp8mm_recipe recipe_a, const float* scale_b,
-                                      fp8mm_recipe recipe_b, const void* bias, fp8mm_out_dtype out_dtype, void* out,
-                                      int64_t ldo, hipStream_t stream) {
+                                      fp8mm_recipe recipe_b, const void* bias, int bias_per_expert,
+                                      fp8mm_out_dtype out_dtype, void* out, int64_t ldo, hipStream_t stream) {
   if (!valid_recipe(recipe_a) || !valid_recipe(recipe_b)) return fail(FP8MM_EINVAL, "unknown recipe value");
+  if (bias_per_expert != 0 && bias_per_expert != 1) return fail(FP8MM_EINVAL, "bias_per_expert must be 0 or 1");
   if (b_layout != FP8MM_B_NK && b_layout != FP8MM_B_KN) return fail(FP8MM_EINVAL, "unknown B layout");
   if (!offsets) return fail(FP8MM_EINVAL, "offsets are required for the grouped GEMM");
   if (out_dtype != FP8MM_OUT_BF16 && out_dtype != FP8MM_OUT_FP32) return fail(FP8MM_EINVAL, "unknown out_dtype");
@@ -321,6 +323,7 @@ fp8mm_status fp8_scaled_grouped_mm_v2(const uint8_t* A, int64_t M_total, int64_t
   p.sa = scale_a;
   p.sb = scale_b;
   p.bias = static_cast<const uint16_t*>(bias);
+  p.bias_stride_e = bias_per_expert ? N : 0;
   p.out = out;
   p.M = M_total;
   p.N = N;

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(WM * WN * 64, GROUPED_K ? 2 : 1) void gemm_kernel(G
     // (rowwise) or grid e of [E, N/128 x K/128] (128x128)
     ti.B = p.B + int64_t(e_found) * p.N * p.K + (B_KN ? ti.n0 : ti.n0 * p.ldb);
     ti.sb = p.sb + int64_t(e_found) * (EPI == Epi::Block128x128 ? (p.N / 128) * (p.K / 128) : p.N);
-    ti.bias = BIAS ? p.bias + int64_t(e_found) * p.N : nullptr;
+    ti.bias = BIAS ? p.bias + int64_t(e_found) * p.bias_stride_e : nullptr;
   }
 
   const int K = ti.K;

@@ -125,9 +125,10 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   // m-tiles of one expert (consecutive g) mostly share its B tiles there too,
   // and the real m-tiles (a prefix of the upper bound the grid is sized for)
   // are spread over all XCDs.
-  // Expert e's B is [N, K] (or [K, N]) at B + e N K, its bias row e of
-  // [E, N], its scales row e of [E, N] (rowwise) or grid e of [E, N/128 x
-  // K/128] (128x128).
+  // Expert e's B is [N, K] (or [K, N]) at B + e N K, its bias the [N] row
+  // at bias + e bias_stride_e (one shared row, or row e of [E, N]), its
+  // scales row e of [E, N] (rowwise) or grid e of [E, N/128 x K/128]
+  // (128x128).
   int tn;
   int64_t row0;
   int rows_valid;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     rows_valid = int(min<int64_t>(SY_BM, rend - row0));
     Bg = p.B + int64_t(e) * p.N * p.K;
     sbg = p.sb + int64_t(e) * (EPI == Epi::Block128x128 ? (p.N / 128) * (p.K / 128) : p.N);
-    if constexpr (BIAS) biasg = p.bias + int64_t(e) * p.N;
+    if constexpr (BIAS) biasg = p.bias + int64_t(e) * p.bias_stride_e;
   } else {
     int tm;
     if (!tile_coords(tiles_m, tiles_n, tm, tn)) return;

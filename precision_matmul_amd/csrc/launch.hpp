@@ -21,7 +21,8 @@ struct GemmProblem {
   const uint8_t* B;
   const float* sa;
   const float* sb;
-  const uint16_t* bias;   // bf16 [N] ([E, N] grouped) or null
+  const uint16_t* bias;   // bf16 [N] or null; grouped: expert e reads bias + e * bias_stride_e
+  int64_t bias_stride_e;  // grouped: 0 (one [N] row for every expert) or N ([E, N])
   void* out;
   int64_t M, N, K;
   int64_t lda, ldb, ldo;

@@ -38,21 +38,26 @@ def _quant_block(bits, block):
     return q, s, rq, rs
 
 
-def _grouped_blockwise_case(E, N, K, sizes, layout, seed, with_bias=False, out_dtype=torch.bfloat16):
+def _grouped_blockwise_case(E, N, K, sizes, layout, seed, bias_form=None, out_dtype=torch.bfloat16):
+    """bias_form: None, "shared" (bf16 [N], every expert) or "per_expert"
+    (bf16 [E, N], row e for expert e)."""
     g = workloads.streams(seed, 3)
     M = int(np.sum(sizes))
     act = workloads.normal_bf16(g[0], (M + 5, K))                 # 5 trailing rows no expert owns
     shape = (E, N, K) if layout == "NK" else (E, K, N)
     W = workloads.normal_bf16(g[1], shape, 0.02)
-    bias = workloads.normal_bf16(g[2], (E, N), 0.5) if with_bias else None
+    bias = None
+    if bias_form is not None:
+        bias = workloads.normal_bf16(g[2], (E, N) if bias_form == "per_expert" else (N,), 0.5)
     offs = np.cumsum(sizes).astype(np.int32)
     qa, sa, ra, rsa = _quant_block(act, (1, 128))
     qw, sw, rw, rsw = _quant_block(W.reshape(E * shape[1], shape[2]), (128, 128))
     grid = sw.shape[0] // E, sw.shape[1]
-    say(f"grouped blockwise E={E} N={N} K={K} {layout} bias={with_bias} {out_dtype}")
+    say(f"grouped blockwise E={E} N={N} K={K} {layout} bias={bias_form} {out_dtype}")
     out = fp8mm.fp8_scaled_grouped_mm_v2(qa, qw.reshape(shape), _offs_dev(offs), sa, "1x128",
                                          sw.reshape((E,) + grid), "128x128", b_layout=layout,
-                                         bias=None if bias is None else bf16_dev(bias), out_dtype=out_dtype)
+                                         bias=None if bias is None else bf16_dev(bias),
+                                         bias_per_expert=bias_form == "per_expert", out_dtype=out_dtype)
     ref, written = gemm.grouped_mm(ra, rw.reshape(shape), offs, rsa, rsw.reshape((E,) + grid),
                                    bias=None if bias is None else quant.bf16_to_f32(bias), out_dtype=None,
                                    recipe_a="1x128", recipe_b="128x128", layout=layout)
@@ -72,11 +77,14 @@ def test_grouped_blockwise(E, N, K, sizes, layout):
     _assert_close(got, ref, f"grouped 1x128 x 128x128 E={E} N={N} K={K} {layout}")
 
 
+@pytest.mark.parametrize("bias_form", ["shared", "per_expert"])
 @pytest.mark.parametrize("layout", ["NK", "KN"])
-def test_grouped_blockwise_bias_fp32(layout):
+def test_grouped_blockwise_bias_fp32(layout, bias_form):
+    """Both bias forms of the grouped call: one [N] row added to every
+    expert's rows, or [E, N] with row e for expert e."""
     got, ref = _grouped_blockwise_case(5, 256, 256, np.array([70, 0, 200, 3, 90]), layout, seed=5,
-                                       with_bias=True, out_dtype=torch.float32)
-    _assert_close(got, ref, f"grouped blockwise bias fp32 {layout}", out_dtype="fp32")
+                                       bias_form=bias_form, out_dtype=torch.float32)
+    _assert_close(got, ref, f"grouped blockwise bias ({bias_form}) fp32 {layout}", out_dtype="fp32")
 
 
 @pytest.mark.parametrize("N", [128, 384])
@@ -110,15 +118,15 @@ def test_grouped_rowwise_short_remainders(N, ld_pad, out_dtype, K):
     to full tiles; N = 406 ends
     the last 256-column tile after 150 columns (a lane's group of four partly
     outside it); out with ld = N or padded (16-byte vector stores where the
-    padding aligns every row); bias per expert; K = 400 ends the last K step
-    after 16 of its 128 bytes."""
+    padding aligns every row); a bias shared by the experts ([N]); K = 400
+    ends the last K step after 16 of its 128 bytes."""
     sizes = np.array([256 + 1, 64, 0, 256 + 63, 65, 17, 256, 256 + 40, 3, 256 + 100, 128, 97])
     E = len(sizes)
     g = workloads.streams(N + ld_pad + K, 3)
     M = int(sizes.sum())
     act = workloads.normal_bf16(g[0], (M + 4, K))                 # 4 trailing rows no expert owns
     W = workloads.normal_bf16(g[1], (E * N, K), 0.02)
-    bias = workloads.normal_bf16(g[2], (E, N), 0.5)
+    bias = workloads.normal_bf16(g[2], (N,), 0.5)
     offs = np.cumsum(sizes).astype(np.int32)
     qa, sa = fp8mm.fp8_quantize_rowwise(bf16_dev(act))
     ra, rsa = quant.quantize_rowwise(act)

@@ -113,10 +113,10 @@ def test_grouped_v2_checks_recipes_and_shapes(lib):
 
     def call(**kw):
         a = dict(A=FAKE, M=64, K=256, B=FAKE, E=4, N=128, layout=0, offs=FAKE, sa=FAKE, ra=2, sb=FAKE, rb=3,
-                 bias=None, od=0, out=FAKE, ldo=128)
+                 bias=None, per_expert=0, od=0, out=FAKE, ldo=128)
         a.update(kw)
         return f(a["A"], a["M"], a["K"], a["B"], a["E"], a["N"], a["layout"], a["offs"], a["sa"], a["ra"], a["sb"],
-                 a["rb"], a["bias"], a["od"], a["out"], a["ldo"], None)
+                 a["rb"], a["bias"], a["per_expert"], a["od"], a["out"], a["ldo"], None)
 
     assert call(offs=None) == _lib.EINVAL
     assert call(ra=0, rb=0) == _lib.ENOTIMPL                   # tensorwise grouped
@@ -132,7 +132,10 @@ def test_grouped_v2_checks_recipes_and_shapes(lib):
     assert call(E=-1) == _lib.EINVAL
     assert call(E=(1 << 16) + 1) == _lib.EINVAL                # expert count cap
     assert "E <= 2^16" in lib.fp8mm_last_error().decode()
+    assert call(per_expert=2) == _lib.EINVAL                   # bias form: 0 ([N]) or 1 ([E, N])
+    assert "bias_per_expert" in lib.fp8mm_last_error().decode()
     assert call(M=0) == _lib.OK                                # empty: nothing to do
+    assert call(M=0, bias=FAKE, per_expert=1) == _lib.OK
 
 
 def test_grouped_weight_gradient_entries_check_capacity(lib):
