@@ -75,9 +75,14 @@ def _ld16(n):
     return max(16, (n + 15) // 16 * 16)
 
 
-def _check_scale(scale, recipe, operand, M, N, K):
-    """The C ABI takes bare pointers, so the element count of each scale
-    array is checked here against its recipe (see fp8mm_recipe)."""
+def _check_scale(scale, recipe, operand, M, N, K, device):
+    """The C ABI takes bare pointers, so each scale array is checked here:
+    a tensor on the operands' device, its dtype and its element count against
+    the recipe (see fp8mm_recipe)."""
+    if not isinstance(scale, torch.Tensor):
+        raise ValueError(f"scale_{operand} must be a torch.Tensor")
+    if scale.device != device:
+        raise ValueError(f"scale_{operand} must be on {device}, got {scale.device}")
     r = _recipe(recipe)
     rows = M if operand == "a" else N
     want = {0: 1, 1: rows}
@@ -180,19 +185,21 @@ def fp8_scaled_mm(A, B, scale_a, recipe_a, scale_b, recipe_b, b_layout="NK", bia
     _need(B, torch.uint8, "B")
     if b_layout not in _lib.B_LAYOUTS:
         raise ValueError(f"b_layout must be 'NK' or 'KN', got {b_layout!r}")
-    if not (scale_a.is_contiguous() and scale_b.is_contiguous()):
-        raise ValueError("scales must be contiguous")
+    if B.device != A.device:
+        raise ValueError(f"B must be on {A.device}, got {B.device}")
     M, K = A.shape
     N = B.shape[0] if b_layout == "NK" else B.shape[1]
     kb = B.shape[1] if b_layout == "NK" else B.shape[0]
     if kb != K:
         raise ValueError(f"contraction mismatch: A has K={K}, B has {kb}")
-    _check_scale(scale_a, recipe_a, "a", M, N, K)
-    _check_scale(scale_b, recipe_b, "b", M, N, K)
+    _check_scale(scale_a, recipe_a, "a", M, N, K, A.device)
+    _check_scale(scale_b, recipe_b, "b", M, N, K, A.device)
+    if not (scale_a.is_contiguous() and scale_b.is_contiguous()):
+        raise ValueError("scales must be contiguous")
     if bias is not None:
         _need(bias, torch.bfloat16, "bias")
-        if bias.numel() != N or not bias.is_contiguous():
-            raise ValueError("bias must be a contiguous bf16 tensor of N elements")
+        if bias.numel() != N or not bias.is_contiguous() or bias.device != A.device:
+            raise ValueError("bias must be a contiguous bf16 tensor of N elements on the operands' device")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=A.device)
     elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or out.device != A.device:
@@ -208,9 +215,9 @@ def fp8_scaled_mm(A, B, scale_a, recipe_a, scale_b, recipe_b, b_layout="NK", bia
 def fp8_scaled_grouped_mm(A, B_EnK, offsets, scale_a, scale_b, bias=None, out_dtype=torch.bfloat16, out=None):
     """Grouped (MoE) GEMM in the form grouped_mm(act, weight.transpose(-2, -1),
     offs): A uint8 [M_total, K], B_EnK uint8 [E, N, K], offsets int32 [E]
-    (cumulative end rows), rowwise scales scale_a [M_total] and scale_b [E, N].
-    Rows at or past offsets[-1] are left as they are in `out` (zeros when the
-    output is allocated here)."""
+    (cumulative end rows), rowwise scales scale_a [M_total] and scale_b [E, N],
+    bias bf16 [N] added to every expert's rows.  Rows at or past offsets[-1]
+    are left as they are in `out` (zeros when the output is allocated here)."""
     if offsets is None:
         raise ValueError("offsets are required for the grouped GEMM")
     _need(A, torch.uint8, "A")
@@ -230,8 +237,8 @@ def fp8_scaled_grouped_mm(A, B_EnK, offsets, scale_a, scale_b, bias=None, out_dt
         raise ValueError("rowwise scales must have M_total and E*N elements")
     if bias is not None:
         _need(bias, torch.bfloat16, "bias")
-        if bias.numel() != E * N or not bias.is_contiguous():
-            raise ValueError("bias must be a contiguous bf16 [E, N] tensor")
+        if bias.numel() != N or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous bf16 tensor of N elements (shared by every expert)")
     if out is None:
         out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
     elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or out.device != A.device:
@@ -244,13 +251,15 @@ def fp8_scaled_grouped_mm(A, B_EnK, offsets, scale_a, scale_b, bias=None, out_dt
 
 
 def fp8_scaled_grouped_mm_v2(A, B_E, offsets, scale_a, recipe_a, scale_b, recipe_b, b_layout="NK", bias=None,
-                             out_dtype=torch.bfloat16, out=None):
+                             bias_per_expert=False, out_dtype=torch.bfloat16, out=None):
     """Grouped (MoE) GEMM with explicit recipes: rows [offsets[e-1],
     offsets[e]) of A [M_total, K] times expert e's B, B_E uint8 [E, N, K]
     (b_layout "NK") or [E, K, N] ("KN").  Pairs: rowwise x rowwise (scale_a
     [M_total], scale_b [E, N]) and 1x128 x 128x128 (scale_a [K/128, M_total],
-    scale_b [E] x expert e's 128x128 grid of B as stored).  Rows at or past
-    offsets[-1] are left as they are in `out` (zeros when allocated here)."""
+    scale_b [E] x expert e's 128x128 grid of B as stored).  bias: bf16 [N]
+    shared by every expert, or [E, N] (row e for expert e) with
+    bias_per_expert=True.  Rows at or past offsets[-1] are left as they are in
+    `out` (zeros when allocated here)."""
     if offsets is None:
         raise ValueError("offsets are required for the grouped GEMM")
     if b_layout not in _lib.B_LAYOUTS:
@@ -283,16 +292,18 @@ def fp8_scaled_grouped_mm_v2(A, B_E, offsets, scale_a, recipe_a, scale_b, recipe
                          f"the recipes need {want_a} and {want_b}")
     if bias is not None:
         _need(bias, torch.bfloat16, "bias")
-        if bias.numel() != E * N or not bias.is_contiguous():
-            raise ValueError("bias must be a contiguous bf16 [E, N] tensor")
+        want = E * N if bias_per_expert else N
+        if bias.numel() != want or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous bf16 tensor of " +
+                             ("[E, N] elements (bias_per_expert)" if bias_per_expert else "N elements"))
     if out is None:
         out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
     elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or out.device != A.device:
         raise ValueError("out has the wrong dtype, shape or device")
     st = _lib.load().fp8_scaled_grouped_mm_v2(A.data_ptr(), M, K, B_E.data_ptr(), E, N, _lib.B_LAYOUTS[b_layout],
                                               offsets.data_ptr(), scale_a.data_ptr(), ra, scale_b.data_ptr(), rb,
-                                              _ptr(bias), _out_code(out_dtype), out.data_ptr(), _ld(out, "out"),
-                                              _stream(A))
+                                              _ptr(bias), int(bool(bias_per_expert)), _out_code(out_dtype),
+                                              out.data_ptr(), _ld(out, "out"), _stream(A))
     _lib.check(st, "fp8_scaled_grouped_mm_v2")
     return out
 
@@ -385,8 +396,8 @@ def fp8_linear_forward(x_q, x_scale, x_recipe, w_q, w_scale, w_recipe, bias=None
             raise ValueError("bias must be a contiguous bf16 tensor of N elements")
     for t, n in ((x_scale, "x_scale"), (w_scale, "w_scale")):
         _need(t, torch.float32, n)
-    _check_scale(x_scale, x_recipe, "a", M, N, K)
-    _check_scale(w_scale, w_recipe, "b", M, N, K)
+    _check_scale(x_scale, x_recipe, "a", M, N, K, x_q.device)
+    _check_scale(w_scale, w_recipe, "b", M, N, K, x_q.device)
     out = torch.empty((M, N), dtype=out_dtype, device=x_q.device)
     st = _lib.load().fp8_linear_forward(x_q.data_ptr(), M, K, x_scale.data_ptr(), _recipe(x_recipe), w_q.data_ptr(),
                                         N, w_scale.data_ptr(), _recipe(w_recipe), _ptr(bias),
@@ -405,8 +416,8 @@ def fp8_linear_grad_input(g_q, g_scale, g_recipe, w_q, w_scale, w_recipe, out_dt
     K_in = w_q.shape[1]
     for t, n in ((g_scale, "g_scale"), (w_scale, "w_scale")):
         _need(t, torch.float32, n)
-    _check_scale(g_scale, g_recipe, "a", M, K_in, N_out)
-    _check_scale(w_scale, w_recipe, "b", M, K_in, N_out)
+    _check_scale(g_scale, g_recipe, "a", M, K_in, N_out, g_q.device)
+    _check_scale(w_scale, w_recipe, "b", M, K_in, N_out, g_q.device)
     out = torch.empty((M, K_in), dtype=out_dtype, device=g_q.device)
     st = _lib.load().fp8_linear_grad_input(g_q.data_ptr(), M, N_out, g_scale.data_ptr(), _recipe(g_recipe),
                                            w_q.data_ptr(), K_in, w_scale.data_ptr(), _recipe(w_recipe),
@@ -426,8 +437,8 @@ def fp8_linear_grad_weight(gt_q, gt_scale, xt_q, xt_scale, out_dtype=torch.bfloa
     K_in = xt_q.shape[0]
     for t, n in ((gt_scale, "gt_scale"), (xt_scale, "xt_scale")):
         _need(t, torch.float32, n)
-    _check_scale(gt_scale, "1x128", "a", N_out, K_in, T)
-    _check_scale(xt_scale, "128x1", "b", N_out, K_in, T)
+    _check_scale(gt_scale, "1x128", "a", N_out, K_in, T, gt_q.device)
+    _check_scale(xt_scale, "128x1", "b", N_out, K_in, T, gt_q.device)
     out = torch.empty((N_out, K_in), dtype=out_dtype, device=gt_q.device)
     st = _lib.load().fp8_linear_grad_weight(gt_q.data_ptr(), N_out, T, gt_scale.data_ptr(), xt_q.data_ptr(), K_in,
                                             xt_scale.data_ptr(), _out_code(out_dtype), out.data_ptr(), _stream(gt_q))

@@ -194,6 +194,52 @@ def test_split_tail_rows(recipe, M, K):
     _assert_close(out_f64(out), ref, f"split tail {recipe} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("recipe", ["blockwise", "grad_input", "rowwise", "mxfp8"])
+def test_split_tail_three_uneven_k_ranges(recipe):
+    """A row tail split along K into three uneven ranges.  M = 3300, 5120
+    output columns: 13 x 20 = 260 tiles of 256 x 256, so on a 256-CU device
+    the streaming kernel takes the 12 tile rows that fill whole rounds (240
+    tiles, rows 0 .. 3071) and the 228 remaining rows (20 tiles of 256 x 256,
+    80 of 128 x 128) are split into min(256 / 80, 25 / 8, 8) = 3 K ranges of
+    8, 8 and 9 steps over the contraction of 3200 (25 steps of 128).  The same
+    split happens at 16640 x 5120 x 8192 (21 / 21 / 22 of 64 steps).  Every
+    element is compared; the rowwise case adds the bias in the reduction."""
+    M, N, K = 3300, 5120, 3200
+    if recipe == "grad_input":
+        # grad_input [M, 5120] = grad_output [M, 3200] @ weight [3200, 5120] (B stored [K, N])
+        inp = workloads.blockwise(M=M, N=K, K=N, seed=91)
+        qg, sg, rg, rsg = _quant_both(inp["grad_output"], "1x128")
+        qw, sw, rw, rsw = _quant_both(inp["weight"], "128x128")
+        out = fp8mm.fp8_linear_grad_input(qg, sg, "1x128", qw, sw, "128x128")
+        ref = gemm.linear_grad_input(rg, rsg, "1x128", rw, rsw, "128x128", out_dtype=None)
+    elif recipe == "blockwise":
+        inp = workloads.blockwise(M=M, N=N, K=K, seed=92)
+        qa, sa, ra, rsa = _quant_both(inp["input"], "1x128")
+        qb, sb, rb, rsb = _quant_both(inp["weight"], "128x128")
+        out = fp8mm.fp8_linear_forward(qa, sa, "1x128", qb, sb, "128x128")
+        ref = gemm.linear_forward(ra, rsa, "1x128", rb, rsb, "128x128", out_dtype=None)
+    elif recipe == "rowwise":
+        inp = workloads.rowwise(M=M, N=N, K=K, seed=93)
+        qa, sa, ra, rsa = _quant_both(inp["x"], "rowwise")
+        qb, sb, rb, rsb = _quant_both(inp["w"], "rowwise")
+        out = fp8mm.fp8_scaled_mm(qa, qb, sa, "rowwise", sb, "rowwise", bias=bf16_dev(inp["bias"]))
+        ref = gemm.scaled_mm(ra, rb, rsa, "rowwise", rsb, "rowwise", bias=quant.bf16_to_f32(inp["bias"]),
+                             out_dtype=None)
+    else:
+        g = workloads.streams(94, 2)
+        x = workloads.normal_bf16(g[0], (M, K))
+        w = workloads.normal_bf16(g[1], (N, K), 0.02)
+        qa, sa = fp8mm.fp8_quantize_mx(bf16_dev(x))
+        qb, sb = fp8mm.fp8_quantize_mx(bf16_dev(w))
+        ra, rsa = mx.quantize_mx(x)
+        rb, rsb = mx.quantize_mx(w)
+        out = fp8mm.fp8_scaled_mm(qa, qb, sa, "mxfp8", sb, "mxfp8")
+        ref = gemm.scaled_mm(ra, rb, rsa, "mxfp8", rsb, "mxfp8", out_dtype=None)
+    got = out_f64(out)
+    _assert_close(got, ref, f"three-way split tail {recipe} {M}x{N}x{K}")
+    _assert_close(got[3072:], ref[3072:], f"three-way split tail {recipe}: the tail rows alone")
+
+
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("pad", [0, 64])
 def test_output_rows_contiguous_or_padded(out_dtype, pad):
@@ -249,7 +295,7 @@ def test_full_mxfp8_sampled():
     qa, sa = fp8mm.fp8_quantize_mx(bf16_dev(x))
     qb, sb = fp8mm.fp8_quantize_mx(bf16_dev(w))
     out = out_f64(fp8mm.fp8_scaled_mm(qa, qb, sa, "mxfp8", sb, "mxfp8"))
-    I = _sample(M, 64, 11)
+    I = _rows_with_tail(M, 48, 16, 11)
     J = _sample(N, 64, 12)
     ra, rsa = mx.quantize_mx(x[I])
     rb, rsb = mx.quantize_mx(w[J])
@@ -257,17 +303,26 @@ def test_full_mxfp8_sampled():
     _assert_close(out[np.ix_(I, J)], ref, "mxfp8 16640x5120x8192 sampled")
 
 
-def _grouped_case(E, N, K, sizes, seed, with_bias=False):
+def _grouped_case(E, N, K, sizes, seed, bias_form=None):
+    """bias_form: None, "shared" (bf16 [N] through fp8_scaled_grouped_mm) or
+    "per_expert" (bf16 [E, N] through fp8_scaled_grouped_mm_v2)."""
     g = workloads.streams(seed, 3)
     M = int(np.sum(sizes))
     act = workloads.normal_bf16(g[0], (M + 7, K))          # 7 trailing rows no expert owns
     W = workloads.normal_bf16(g[1], (E, N, K), 0.02)
-    bias = workloads.normal_bf16(g[2], (E, N), 0.5) if with_bias else None
+    bias = None
+    if bias_form is not None:
+        bias = workloads.normal_bf16(g[2], (E, N) if bias_form == "per_expert" else (N,), 0.5)
     offs = np.cumsum(sizes).astype(np.int32)
     qa, sa, ra, rsa = _quant_both(act, "rowwise")
     qw, sw, rw, rsw = _quant_both(W.reshape(E * N, K), "rowwise")
-    out = fp8mm.fp8_scaled_grouped_mm(qa, qw.reshape(E, N, K), torch.from_numpy(offs).cuda(), sa,
-                                      sw.reshape(E, N), bias=None if bias is None else bf16_dev(bias))
+    if bias_form == "per_expert":
+        out = fp8mm.fp8_scaled_grouped_mm_v2(qa, qw.reshape(E, N, K), torch.from_numpy(offs).cuda(), sa.reshape(-1),
+                                             "rowwise", sw.reshape(-1), "rowwise", bias=bf16_dev(bias),
+                                             bias_per_expert=True)
+    else:
+        out = fp8mm.fp8_scaled_grouped_mm(qa, qw.reshape(E, N, K), torch.from_numpy(offs).cuda(), sa,
+                                          sw.reshape(E, N), bias=None if bias is None else bf16_dev(bias))
     ref, written = gemm.grouped_mm(ra, rw.reshape(E, N, K), offs, rsa, rsw.reshape(E, N),
                                    bias=None if bias is None else quant.bf16_to_f32(bias), out_dtype=None)
     got = out_f64(out)
@@ -282,10 +337,10 @@ def _grouped_case(E, N, K, sizes, seed, with_bias=False):
     (70, 64, 128, [3] * 70),
     (4, 128, 64, [10, 50, 0, 70]),                       # K below 128 bytes: 128 x 128 tiles
     (16, 384, 1024, [300, 257, 256, 255, 1, 0, 512, 40, 290, 310, 222, 260, 275, 233, 249, 301])])
-@pytest.mark.parametrize("with_bias", [False, True])
-def test_grouped_rowwise(E, N, K, sizes, with_bias):
-    got, ref = _grouped_case(E, N, K, np.array(sizes), seed=E + N + K, with_bias=with_bias)
-    _assert_close(got, ref, f"grouped E={E} N={N} K={K} bias={with_bias}")
+@pytest.mark.parametrize("bias_form", [None, "shared", "per_expert"])
+def test_grouped_rowwise(E, N, K, sizes, bias_form):
+    got, ref = _grouped_case(E, N, K, np.array(sizes), seed=E + N + K, bias_form=bias_form)
+    _assert_close(got, ref, f"grouped E={E} N={N} K={K} bias={bias_form}")
 
 
 def test_grouped_single_expert_equals_rowwise_gemm():
@@ -316,6 +371,24 @@ def test_zero_sized_problems():
     assert torch.count_nonzero(out).item() == 0
 
 
+def test_host_scale_tensors_are_rejected():
+    """The ABI takes bare device pointers: a scale (or bias) in host memory
+    must be refused with ValueError before anything is launched."""
+    a = torch.zeros((256, 256), dtype=torch.uint8, device="cuda")
+    dev_one = torch.ones((1, 1), dtype=torch.float32, device="cuda")
+    host_one = torch.ones((1, 1), dtype=torch.float32)
+    with pytest.raises(ValueError, match="scale_a"):
+        fp8mm.fp8_scaled_mm(a, a, host_one, "tensorwise", dev_one, "tensorwise")
+    with pytest.raises(ValueError, match="scale_b"):
+        fp8mm.fp8_scaled_mm(a, a, dev_one, "tensorwise", host_one, "tensorwise")
+    with pytest.raises(ValueError, match="x_scale"):
+        fp8mm.fp8_linear_forward(a, host_one, "tensorwise", a, dev_one, "tensorwise")
+    with pytest.raises(ValueError, match="bias"):
+        fp8mm.fp8_scaled_mm(a, a, dev_one, "tensorwise", dev_one, "tensorwise",
+                            bias=torch.zeros(256, dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+
+
 def test_unsupported_pair_raises_not_implemented():
     a = torch.zeros((128, 128), dtype=torch.uint8, device="cuda")
     s = torch.ones((128, 1), dtype=torch.float32, device="cuda")
@@ -343,6 +416,19 @@ def test_full_rowwise_linear_sampled():
     _assert_close(got[np.ix_(I, J)], ref, "rowwise 8192x4096x4096 sampled")
 
 
+def _rows_with_tail(M, count, tail_count, seed):
+    """Sampled output rows: `count` from the rows the 256 x 256 streaming
+    tiles cover and `tail_count` from the row tail.  At M = 16640 with N of
+    5120 or 8192 on a 256-CU device the tiles fill exactly 5 or 8 rounds with
+    rows 0 .. 16383, and rows 16384 .. 16639 run on the 128 x 128 tail tiles,
+    split along K (3 uneven ranges of 21 / 21 / 22 K steps when the output
+    has 20 tile columns and K = 8192, 2 even ones otherwise) and summed by the
+    reduction kernel."""
+    assert M == 16640
+    head = 16384
+    return np.concatenate([_sample(head, count, seed), head + _sample(M - head, tail_count, seed + 100)])
+
+
 @pytest.mark.parametrize("M,N,K", [(16640, 5120, 8192), (16640, 8192, 5120)])
 def test_full_blockwise_forward_and_grad_input_sampled(M, N, K):
     inp = workloads.blockwise(M=M, N=N, K=K)
@@ -350,7 +436,8 @@ def test_full_blockwise_forward_and_grad_input_sampled(M, N, K):
     qx, sx = fp8mm.fp8_quantize_blockwise(bf16_dev(x), (1, 128))
     qw, sw = fp8mm.fp8_quantize_blockwise(bf16_dev(w), (128, 128))
     fwd = out_f64(fp8mm.fp8_linear_forward(qx, sx, "1x128", qw, sw, "128x128"))
-    I = _sample(M, 48, 3)
+    I = _rows_with_tail(M, 40, 16, 3)
+    assert np.sum(I >= 16384) == 16
     slabs = _sample(N // 128, 3, 4)
     J = np.concatenate([s * 128 + _sample(128, 16, 5 + s) for s in slabs])
     rqx, rsx = quant.quantize_blockwise(x[I], 1, 128)
