@@ -761,8 +761,11 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t st) {
     return p.out_bf16 ? launch_group_k<true>(p, st) : launch_group_k<false>(p, st);
   }
   if (p.offsets) {
-    // grouped: the streaming kernel when its grouped loads fit the leading
-    // dimensions (as below), else 128 x 128 tiles
+    // grouped: experts of a few hundred rows with weights stored [N, K] on
+    // the weight-streaming kernel; otherwise the streaming kernel when its
+    // grouped loads fit the leading dimensions (as below), else 128 x 128
+    // tiles
+    if (grouped_wide_applies(p)) return launch_gemm_grouped_wide(p, st);
     if (p.lda >= 128 && (p.b_kn ? p.ldb >= 256 : p.ldb >= 128)) return launch_gemm_streaming(p, st);
     if (p.epi == Epi::Row)
       return p.b_kn ? launch_out<Epi::Row, true, true>(p, st) : launch_out<Epi::Row, false, true>(p, st);

@@ -56,5 +56,10 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t st);
 hipError_t launch_gemm_streaming(const GemmProblem& p, hipStream_t st);
 // The grouped weight gradient (group_k) on the streaming kernel's 256 x 256 tiles.
 hipError_t launch_gemm_group_k_streaming(const GemmProblem& p, hipStream_t st);
+// Grouped GEMMs in the weight-streaming regime (experts of a few hundred
+// rows, weights stored [N, K]): 320-row m-blocks, one per expert up to 320
+// rows, so each weight slice is read about once.
+bool grouped_wide_applies(const GemmProblem& p);
+hipError_t launch_gemm_grouped_wide(const GemmProblem& p, hipStream_t st);
 
 }  // namespace fp8mm

@@ -336,7 +336,12 @@ def _grouped_case(E, N, K, sizes, seed, bias_form=None):
     (1, 128, 256, [333]),
     (70, 64, 128, [3] * 70),
     (4, 128, 64, [10, 50, 0, 70]),                       # K below 128 bytes: 128 x 128 tiles
-    (16, 384, 1024, [300, 257, 256, 255, 1, 0, 512, 40, 290, 310, 222, 260, 275, 233, 249, 301])])
+    (16, 384, 1024, [300, 257, 256, 255, 1, 0, 512, 40, 290, 310, 222, 260, 275, 233, 249, 301]),
+    # experts of 800 rows on average: the 256 x 256 streaming tiles (the
+    # cases above have at most 384 rows per expert on average and take the
+    # 320-row weight-streaming kernel)
+    (2, 256, 512, [700, 900]),
+    (3, 400, 384, [1000, 0, 700])])
 @pytest.mark.parametrize("bias_form", [None, "shared", "per_expert"])
 def test_grouped_rowwise(E, N, K, sizes, bias_form):
     got, ref = _grouped_case(E, N, K, np.array(sizes), seed=E + N + K, bias_form=bias_form)

@@ -71,7 +71,9 @@ def _grouped_blockwise_case(E, N, K, sizes, layout, seed, bias_form=None, out_dt
     (8, 256, 512, [100, 0, 300, 1, 129, 0, 0, 256]),
     (3, 128, 256, [5, 260, 64]),                 # N = 128: B stored [K, N] takes 128 x 128 tiles
     (1, 384, 384, [333]),
-    (16, 384, 1024, [300, 257, 256, 255, 1, 0, 512, 40, 290, 310, 222, 260, 275, 233, 249, 301])])
+    (16, 384, 1024, [300, 257, 256, 255, 1, 0, 512, 40, 290, 310, 222, 260, 275, 233, 249, 301]),
+    (2, 512, 512, [700, 900]),                  # experts of 800 rows: the 256 x 256 streaming tiles
+    (6, 1408, 512, [320, 321, 0, 640, 1, 319])])   # N = 1408: eight 176-column n-blocks; m-block edges
 def test_grouped_blockwise(E, N, K, sizes, layout):
     got, ref = _grouped_blockwise_case(E, N, K, np.array(sizes), layout, seed=E + N + K)
     _assert_close(got, ref, f"grouped 1x128 x 128x128 E={E} N={N} K={K} {layout}")
