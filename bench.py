@@ -1,7 +1,7 @@
 """Benchmark of the FP8 scaled-GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-recipes] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
+                    [--no-cpu-baseline] [--no-recipes] [--workload NAME]
 
 One step = one pass of the whole hot path over the workload's synthetic
 inputs (already resident in HBM): dynamic quantization of both operands
@@ -36,11 +36,16 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GEMM's time falls for its first ~60 calls on a fresh process (0.75
-    # -> 0.57 ms at 16640x5120x8192, with or without the quantizes between
-    # them) before it settles: 100 untimed steps reach the settled state.
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    # On a fresh load the device's power controller first lets the shader
+    # clock run (1.77 GHz for the first two GEMM calls), then pulls it down
+    # (1.61 GHz at calls 3-5) and takes about 30 calls (40 ms) of back-to-back
+    # steps to settle at its sustained clock (1.83 GHz); the GEMM's cycle
+    # count stays the same throughout, so its time follows the clock.  The
+    # settle phase runs the step back to back for this long before the
+    # warm-up steps, so the timed steps see the sustained clock.
+    ap.add_argument("--settle-ms", type=float, default=200.0)
     ap.add_argument("--workload", default="blockwise_fwd_16640x5120x8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-recipes", action="store_true")
@@ -279,15 +284,23 @@ def time_kernel(torch, fn, iters, warmup=3):
     return t[len(t) // 2], float(np.mean(t)), t[0], t[-1]
 
 
-def time_cold(torch, fn, flush, iters=20, warmup=3):
+def time_cold(torch, fn, flush, iters=20, warmup=3, clean=True):
     """Device time (ms) of fn with HBM-resident operands: before each timed
-    call a 512 MiB buffer (twice the 256 MiB MALL) is overwritten outside
-    the events.  (median, min, max)."""
+    call a 512 MiB buffer (twice the 256 MiB MALL) is overwritten outside the
+    events, then (clean) a second 512 MiB buffer is read, also outside the
+    events.  The read evicts the overwritten lines, so their write-back to
+    HBM happens before the timed call instead of inside it, and leaves clean
+    lines of other data in the caches: the timed call reads its operands
+    from HBM and pays for no one else's writes.  clean=False times the call
+    right after the overwrite (caches full of dirty lines).  (median, min,
+    max)."""
     for _ in range(warmup):
         fn()
     t = []
     for _ in range(iters):
-        flush.fill_(1)
+        flush[0].fill_(1)
+        if clean:
+            flush[1].view(torch.int32).max()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         fn()
@@ -338,29 +351,35 @@ def cpu_baseline(workloads):
     from oracle import gemm as ogemm
     from oracle import quant as oquant
 
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     Ms, N, K = 16640, 5120, 8192
     inp = workloads.blockwise(M=16640, N=N, K=K)
     x = inp["input"][:Ms]
     w = inp["weight"]
-    t0 = time.perf_counter()
-    qx, sx = oquant.quantize_blockwise(x, 1, 128)
-    qw, sw = oquant.quantize_blockwise(w, 128, 128)
-    ogemm.scaled_mm(qx, qw, sx, "1x128", sw, "128x128")
-    dt = time.perf_counter() - t0
+    # every host core this process may run on, set explicitly on the BLAS
+    # library numpy uses (the oracle's only multi-threaded step is its matmul)
     cores = len(os.sched_getaffinity(0))
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:
-        threads = cores
-    return {"value": round(2.0 * Ms * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(min(cores, threads)),
+    with threadpool_limits(limits=cores, user_api="blas"):
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        t0 = time.perf_counter()
+        qx, sx = oquant.quantize_blockwise(x, 1, 128)
+        qw, sw = oquant.quantize_blockwise(w, 128, 128)
+        ogemm.scaled_mm(qx, qw, sx, "1x128", sw, "128x128")
+        dt = time.perf_counter() - t0
+    threads = max((i.get("num_threads", 1) for i in blas), default=1)
+    lib = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({os.path.basename(i.get('filepath', ''))})"
+                    for i in blas) or "none found"
+    print(f"[bench] cpu baseline: {cores} cores, BLAS {lib}, {threads} threads", file=sys.stderr, flush=True)
+    return {"value": round(2.0 * Ms * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "host_cores_available": cores, "blas": lib, "blas_threads": int(threads),
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"the whole blockwise 1x128_128x128 forward step at {Ms}x{N}x{K}: numpy oracle "
                       f"quantization of the input and the weight, float64 GEMM ({2.0 * Ms * N * K / 1e9:.0f} "
                       f"GFLOP), rounding to bf16"}
 
 
-GEMM_SOURCES = ("gemm.hip", "gemm_sym.hip", "gemm_common.hpp", "grouped.hpp", "launch.hpp")
+GEMM_SOURCES = ("gemm.hip", "gemm_sym.hip", "gemm_grp.hip", "gemm_common.hpp", "grouped.hpp", "launch.hpp")
 
 
 def gemm_source_sha():
@@ -429,6 +448,15 @@ def main():
         wl["quant"]()
         return wl["gemm"]()
 
+    settle_steps = 0
+    t_settle = time.perf_counter() + args.settle_ms * 1e-3
+    while args.settle_ms > 0:
+        step()
+        settle_steps += 1
+        if settle_steps % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() >= t_settle:
+                break
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -464,6 +492,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": settle_steps,
+                   "why": "untimed back-to-back steps before the warm-up steps, until the device's power "
+                          "controller has settled the shader clock after its fresh-load transient"},
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -486,7 +517,8 @@ def main():
     if not args.no_recipes:
         copy_gbs = copy_ceiling_gbps(torch)
         result["copy_ceiling_GBps"] = round(copy_gbs, 1)
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        flush = (torch.empty(512 << 20, dtype=torch.uint8, device="cuda"),
+                 torch.ones(512 << 20, dtype=torch.uint8, device="cuda"))
         per = {}
         for name, make in W.items():
             print(f"[bench] recipe workload {name}", file=sys.stderr, flush=True)
@@ -497,12 +529,20 @@ def main():
             q_gbs = w2["quant_bytes"] / (q_med * 1e-3) / 1e9
             g_graph = time_graph(torch, w2["gemm"])
             c_med, c_min, c_max = time_cold(torch, w2["gemm"], flush)
-            per[name] = {"recipe": w2["recipe"], "gemm_ms": round(g_med, 4),
-                         "gemm_ms_min_max": [round(g_min, 4), round(g_max, 4)],
-                         "gemm_ms_graph": None if g_graph is None else round(g_graph, 4),
+            d_med, _, _ = time_cold(torch, w2["gemm"], flush, clean=False)
+            # Primary figures: cold, operands read from HBM (time_cold);
+            # warm (back to back, the operands possibly still in the 256 MiB
+            # MALL) and cold with the caches full of another kernel's dirty
+            # lines beside them.
+            per[name] = {"recipe": w2["recipe"],
                          "gemm_ms_cold": round(c_med, 4), "gemm_ms_cold_min_max": [round(c_min, 4), round(c_max, 4)],
-                         "gemm_tflops": round(w2["flops"] / (g_med * 1e-3) / 1e12, 2),
-                         "gemm_frac_fp8_peak": round(w2["flops"] / (g_med * 1e-3) / 1e12 / FP8_DENSE_PEAK_TFLOPS, 4),
+                         "gemm_ms_cold_dirty_cache": round(d_med, 4),
+                         "gemm_tflops": round(w2["flops"] / (c_med * 1e-3) / 1e12, 2),
+                         "gemm_frac_fp8_peak": round(w2["flops"] / (c_med * 1e-3) / 1e12 / FP8_DENSE_PEAK_TFLOPS, 4),
+                         "gemm_ms_warm": round(g_med, 4),
+                         "gemm_ms_warm_min_max": [round(g_min, 4), round(g_max, 4)],
+                         "gemm_ms_graph_warm": None if g_graph is None else round(g_graph, 4),
+                         "gemm_tflops_warm": round(w2["flops"] / (g_med * 1e-3) / 1e12, 2),
                          "quant_ms": round(q_med, 4),
                          "quant_ms_min_max": [round(q_min, 4), round(q_max, 4)],
                          "quant_GBps": round(q_gbs, 1),
@@ -511,7 +551,9 @@ def main():
             # HBM-bound GEMMs (the grouped MoE shape): the fraction of the
             # attainable roofline, min(peak flops, bytes at 8 TB/s)
             t_roof = max(w2["flops"] / (FP8_DENSE_PEAK_TFLOPS * 1e12), w2["gemm_bytes"] / (HBM_PEAK_GBS * 1e9))
-            per[name]["gemm_frac_attainable_roofline"] = round(t_roof / (g_med * 1e-3), 4)
+            per[name]["gemm_bound"] = "mfma" if w2["flops"] / (FP8_DENSE_PEAK_TFLOPS * 1e12) >= t_roof else "hbm"
+            per[name]["gemm_frac_attainable_roofline"] = round(t_roof / (c_med * 1e-3), 4)
+            per[name]["gemm_frac_attainable_roofline_warm"] = round(t_roof / (g_med * 1e-3), 4)
             if w2 is not wl:
                 del w2
             torch.cuda.empty_cache()
