@@ -46,6 +46,11 @@ def parse():
     # settle phase runs the step back to back for this long before the
     # warm-up steps, so the timed steps see the sustained clock.
     ap.add_argument("--settle-ms", type=float, default=200.0)
+    # The GEMM operands' codes: the quantizers' output (default), or, keeping
+    # shapes, scales and every instruction of the step, all 0x00 (zero) or all
+    # 0x38 (1.0).  Shows how far the device clock, hence the GEMM's rate,
+    # follows the switching activity of the data under the power limit.
+    ap.add_argument("--codes", choices=("quantized", "zero", "one"), default="quantized")
     ap.add_argument("--workload", default="blockwise_fwd_16640x5120x8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-recipes", action="store_true")
@@ -79,7 +84,7 @@ def build_workloads(torch, fp8mm, workloads):
         def gemm():
             return fp8mm.fp8_scaled_mm(state["qx"], state["qw"], state["sx"], "1x128", state["sw"], "128x128")
 
-        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+        return dict(quant=quant, gemm=gemm, state=state, flops=2.0 * M * N * K,
                     gemm_bytes=M * K + N * K + 4 * (K // 128) * (M + N // 128) + 2 * M * N,
                     quant_bytes=3 * (M * K + N * K) + 4 * ((K // 128) * M + (N // 128) * (K // 128)),
                     shape=(M, N, K), recipe="blockwise_1x128_128x128")
@@ -97,7 +102,7 @@ def build_workloads(torch, fp8mm, workloads):
         def gemm():
             return fp8mm.fp8_linear_grad_input(state["qg"], state["sg"], "1x128", state["qw"], state["sw"], "128x128")
 
-        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+        return dict(quant=quant, gemm=gemm, state=state, flops=2.0 * M * N * K,
                     gemm_bytes=M * N + N * K + 4 * (N // 128) * (M + K // 128) + 2 * M * K,
                     quant_bytes=3 * (M * N + N * K), shape=(M, K, N), recipe="blockwise_1x128_128x128 (KN)")
 
@@ -113,7 +118,7 @@ def build_workloads(torch, fp8mm, workloads):
         def gemm():
             return fp8mm.fp8_linear_grad_weight(state["qg"], state["sg"], state["qx"], state["sx"])
 
-        return dict(quant=quant, gemm=gemm, flops=2.0 * T * N_out * K_in,
+        return dict(quant=quant, gemm=gemm, state=state, flops=2.0 * T * N_out * K_in,
                     gemm_bytes=T * (N_out + K_in) + 4 * (T // 128) * (N_out + K_in) + 2 * N_out * K_in,
                     quant_bytes=3 * T * (N_out + K_in), shape=(N_out, K_in, T), recipe="blockwise_1x128_128x1")
 
@@ -129,7 +134,7 @@ def build_workloads(torch, fp8mm, workloads):
         def gemm():
             return fp8mm.fp8_scaled_mm(state["qx"], state["qw"], state["sx"], "rowwise", state["sw"], "rowwise", bias=b)
 
-        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+        return dict(quant=quant, gemm=gemm, state=state, flops=2.0 * M * N * K,
                     gemm_bytes=M * K + N * K + 4 * (M + N) + 2 * N + 2 * M * N,
                     quant_bytes=3 * (M * K + N * K) + 4 * (M + N), shape=(M, N, K), recipe="rowwise_rowwise")
 
@@ -146,7 +151,7 @@ def build_workloads(torch, fp8mm, workloads):
         def gemm():
             return fp8mm.fp8_scaled_mm(state["qx"], state["qw"], state["sx"], "mxfp8", state["sw"], "mxfp8")
 
-        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+        return dict(quant=quant, gemm=gemm, state=state, flops=2.0 * M * N * K,
                     gemm_bytes=M * K + N * K + (M + N) * (K // 32) + 2 * M * N,
                     quant_bytes=3 * (M * K + N * K) + (M + N) * (K // 32), shape=(M, N, K), recipe="mxfp8_mxfp8")
 
@@ -162,7 +167,7 @@ def build_workloads(torch, fp8mm, workloads):
         def gemm():
             return fp8mm.fp8_scaled_mm(state["qa"], state["qb"], state["sa"], "tensorwise", state["sb"], "tensorwise")
 
-        return dict(quant=quant, gemm=gemm, flops=2.0 * n ** 3, gemm_bytes=2 * n * n + 8 + 2 * n * n,
+        return dict(quant=quant, gemm=gemm, state=state, flops=2.0 * n ** 3, gemm_bytes=2 * n * n + 8 + 2 * n * n,
                     quant_bytes=6 * n * n, shape=(n, n, n), recipe="tensorwise_tensorwise")
 
     def grouped():
@@ -183,7 +188,7 @@ def build_workloads(torch, fp8mm, workloads):
             return fp8mm.fp8_scaled_grouped_mm(state["qa"], state["qw"].view(E, N, K), offs, state["sa"],
                                                state["sw"].view(E, N), out=out)
 
-        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+        return dict(quant=quant, gemm=gemm, state=state, flops=2.0 * M * N * K,
                     gemm_bytes=M * K + E * N * K + 4 * (M + E * N) + 4 * E + 2 * M * N,
                     quant_bytes=3 * (M * K + E * N * K) + 4 * (M + E * N), shape=(M, N, K, E),
                     recipe="grouped_rowwise_E64")
@@ -212,7 +217,7 @@ def build_workloads(torch, fp8mm, workloads):
                                                   b_layout=layout, out=out)
 
         scales = 4 * ((K // 128) * M + E * (Nw // 128) * (Kw // 128))
-        return dict(quant=quant, gemm=gemm, flops=2.0 * M * N * K,
+        return dict(quant=quant, gemm=gemm, state=state, flops=2.0 * M * N * K,
                     gemm_bytes=M * K + E * N * K + scales + 4 * E + 2 * M * N,
                     quant_bytes=3 * (M * K + E * N * K) + scales, shape=(M, N, K, E),
                     recipe="grouped_blockwise_1x128_128x128" + (" (KN)" if layout == "KN" else ""))
@@ -236,7 +241,7 @@ def build_workloads(torch, fp8mm, workloads):
             return fp8mm.fp8_grouped_linear_grad_weight(state["qg"], state["sg"], state["qx"], state["sx"], offs, T)
 
         scales = 4 * runs * (N_out + K_in)
-        return dict(quant=quant, gemm=gemm, flops=2.0 * T * N_out * K_in,
+        return dict(quant=quant, gemm=gemm, state=state, flops=2.0 * T * N_out * K_in,
                     gemm_bytes=T * (N_out + K_in) + scales + 4 * E + 2 * E * N_out * K_in,
                     quant_bytes=3 * T * (N_out + K_in) + scales, shape=(N_out, K_in, T, E),
                     recipe="grouped_weight_gradient_1x128_128x1")
@@ -444,6 +449,20 @@ def main():
     wl = W[args.workload]()
     torch.cuda.synchronize()
 
+    if args.codes != "quantized":
+        # quantize once, then pin the GEMM operands to constant codes: the
+        # step still runs the quantizers (into fresh buffers) and the GEMM
+        quant0 = wl["quant"]
+        quant0()
+        state = wl["state"]
+        code = 0 if args.codes == "zero" else 0x38
+        fixed = {k: (torch.full_like(v, code) if k.startswith("q") else v) for k, v in state.items()}
+
+        def quant_fixed():
+            quant0()
+            state.update(fixed)
+        wl["quant"] = quant_fixed
+
     def step():
         wl["quant"]()
         return wl["gemm"]()
@@ -500,7 +519,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8e4m3",
-        "data": "synthetic (seeded bf16 normals, shapes of the method's benchmarks)",
+        "data": "synthetic (seeded bf16 normals, shapes of the method's benchmarks)" if args.codes == "quantized" else
+                f"synthetic shapes; GEMM operand codes replaced by constant {args.codes} codes (clock study, not a "
+                "benchmark figure)",
         "config": {"workload": args.workload, "recipe": wl["recipe"], "shape_MNK": list(wl["shape"]),
                    "step": "quantize both operands + scaled GEMM, bf16 out", "out_dtype": "bf16"},
         "roofline": {"bound": "mfma", "kernel": "GEMM call, " + wl["recipe"] + ": " + (call_kernels or "see profile"),

@@ -272,6 +272,20 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
   // wave waits for all but its newest three loads (the weights of kt+2), so
   // A of kt+1 and the weights of kt+1 (issued a step earlier) have landed,
   // and the barrier makes them visible to every wave.
+  // Rowwise: the epilogue's scales go to LDS now, long before they are
+  // needed, into the A stages' blockwise scale regions (unused by this
+  // recipe): the column scales sB[e, n0 .. n0 + bn) into stage 0's (waves
+  // 0-2, 64 floats each), the row scales sA[row0 .. row0 + 320) into stage
+  // 1's (waves 3-7).  Entries past the tile's rows or columns read zeros.
+  if constexpr (EPI == Epi::Row) {
+    if (wave < 3) {
+      const Rsrc r2 = make_rsrc4(sbe + n0, uint32_t(cols_valid) * 4u);
+      dma_b32(r2, ldsA + GW_A + wave * 256, uint32_t(wave * 64 + lane) * 4u);
+    } else {
+      const Rsrc r2 = make_rsrc4(p.sa + row0, uint32_t(rows_valid) * 4u);
+      dma_b32(r2, ldsA + GW_ASTAGE_PAD + GW_A + (wave - 3) * 256, uint32_t((wave - 3) * 64 + lane) * 4u);
+    }
+  }
   issue_a(0);
   issue_b(0);
   issue_b(1);
@@ -303,13 +317,19 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
   constexpr int PITCH = PW * OUTB + 16;               // padded staging row (bytes)
   static_assert(GW_MB * PITCH <= 2 * GW_ASTAGE_PAD + 3 * GW_B, "staging fits the LDS");
   constexpr int CPR_MAX = PW * OUTB / 16;             // 16-byte chunks per staged row
+  // Rowwise scales from LDS (loaded in the prologue), into registers before
+  // the staging area overwrites them.
   [[maybe_unused]] float sr[GW_RF];
+  [[maybe_unused]] float scol[GW_CF][4];
   if constexpr (EPI == Epi::Row) {
+    const float* lsb = reinterpret_cast<const float*>(smem + GW_A);
+    const float* lsa = reinterpret_cast<const float*>(smem + GW_ASTAGE_PAD + GW_A);
 #pragma unroll
-    for (int i = 0; i < GW_RF; ++i) {
-      const int rt = 16 * (rg + 4 * i) + frow;
-      sr[i] = rt < rows_valid ? p.sa[row0 + rt] : 0.f;
-    }
+    for (int i = 0; i < GW_RF; ++i) sr[i] = lsa[16 * (rg + 4 * i) + frow];
+#pragma unroll
+    for (int j = 0; j < GW_CF; ++j)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) scol[j][cc] = lsb[col_base + 16 * j + 4 * fq + cc];
   }
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
@@ -322,9 +342,9 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          if (c + cc < cols_valid) {
-            if constexpr (EPI == Epi::Row) sc[cc] = sbe[n0 + c + cc];
-            if constexpr (BIAS) bv[cc] = __uint_as_float(uint32_t(biase[n0 + c + cc]) << 16);
+          if constexpr (EPI == Epi::Row) sc[cc] = scol[j][cc];
+          if constexpr (BIAS) {
+            if (c + cc < cols_valid) bv[cc] = __uint_as_float(uint32_t(biase[n0 + c + cc]) << 16);
           }
         }
 #pragma unroll
