@@ -308,10 +308,10 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
   // ---------------- epilogue: scales, bias, one rounding, staged stores ----------------
   // The tile's outputs go through LDS (free after the K loop) so that whole
   // rows leave in 16-byte stores from consecutive lanes: full 128-byte lines
-  // per 8 lanes.  (Stores straight from the fragment layout write 32 bytes
-  // per row per instruction, and the memory side then writes about twice
-  // the output's bytes.)  bf16: the whole 320 x 192 tile in one pass; fp32:
-  // one pass per column group (96 columns).
+  // per 8 lanes.  (Non-temporal stores straight from the fragment layout, 32
+  // bytes per row per instruction, wrote about twice the output's bytes.)
+  // bf16: the whole 320 x 192 tile in one pass; fp32: one pass per column
+  // group (96 columns).
   constexpr int PASSES = OUT_BF16 ? 1 : 2;
   constexpr int PW = GW_BN / PASSES;                  // columns per pass
   constexpr int PITCH = PW * OUTB + 16;               // padded staging row (bytes)
@@ -382,7 +382,9 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
         uint8_t* dst = reinterpret_cast<uint8_t*>(p.out) + ((row0 + rt) * p.ldo + n0 + pc0) * OUTB + ch * 16;
         const int nvals = min(16 / OUTB, pcols - ch * (16 / OUTB));
         if (vec_out && nvals == 16 / OUTB) {
-          __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(src), reinterpret_cast<v4i*>(dst));
+          // plain stores: L2 merges the partial lines at the n-block edges
+          // (non-temporal ones wrote 51 MB for the 46 MB MoE output)
+          *reinterpret_cast<v4i*>(dst) = *reinterpret_cast<const v4i*>(src);
         } else {
           for (int e2 = 0; e2 < nvals; ++e2) {
             if constexpr (OUT_BF16)
