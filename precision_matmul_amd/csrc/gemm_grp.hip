@@ -126,19 +126,22 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
   // n0 / 128 + l (l < 3 used) of expert e.
   [[maybe_unused]] const int64_t nkb = p.K / 128;
   [[maybe_unused]] const int64_t blk0 = n0 / 128;
-  auto issue_a = [&](int kt) {
+  // A load q (q < 5) of K step kt into A slot kt % 2: tile rows 40 w + 8 q
+  // .. +7.  Rows wholly past the m-block are not loaded: their LDS rows feed
+  // only accumulators that are never stored.  The last load of a step also
+  // brings its blockwise scales.
+  auto load_a = [&](int kt, int q) {
     const int s = kt & 1;
     const bool live = kt < nk;
     const uint32_t k0 = uint32_t(kt) * BK;
-    const Rsrc ra = live ? rsA : dead(rsA);
-#pragma unroll
-    for (int q = 0; q < GW_LA; ++q) {
+    if (wave * 40 + q * 8 < rows_valid) {
+      const Rsrc ra = live ? rsA : dead(rsA);
       const int ch = ((q + wave) & 1) ? ch_odd : ch_even;
       uint32_t vo = rowA + uint32_t(q * 8) * uint32_t(p.lda) + uint32_t(ch * 16);
       if (!K_ALIGNED && int(k0) + ch * 16 >= K) vo = 0x80000000u;
       dma_b128(ra, ldsA + s * GW_ASTAGE_PAD + (wave * 40 + q * 8) * 128, vo, k0);
     }
-    if constexpr (BLOCKWISE) {
+    if (BLOCKWISE && q == GW_LA - 1) {
       const uint32_t sc = ldsA + s * GW_ASTAGE_PAD + GW_A;
       if (wave < 5) {
         const int64_t off = int64_t(kt) * p.M + row0 + wave * 64;
@@ -152,21 +155,36 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
       }
     }
   };
-  // The weight loads of K step kt into ring slot kt % 3.  Past the last step
-  // they go through a descriptor with no valid bytes (zeros into a slot
-  // nobody reads), so that every step issues the same three loads last and
-  // one vmcnt immediate tracks the ring.
-  auto issue_b = [&](int kt) {
+  // Weight load q (q < 3) of K step kt into ring slot kt % 3: n-block
+  // columns 24 w + 8 q .. +7.  Past the last step the loads go through a
+  // descriptor with no valid bytes (zeros into a slot nobody reads), so that
+  // every step issues the same three loads last and one vmcnt immediate
+  // tracks the ring.
+  auto load_b = [&](int kt, int q) {
     const int s = kt % 3;
     const uint32_t k0 = uint32_t(kt) * BK;
     const Rsrc rb = kt < nk ? rsB : dead(rsB);
+    const int ch = ((q + wave) & 1) ? ch_odd : ch_even;
+    uint32_t vo = rowB + uint32_t(q * 8) * uint32_t(p.ldb) + uint32_t(ch * 16);
+    if (!K_ALIGNED && int(k0) + ch * 16 >= K) vo = 0x80000000u;
+    dma_b128(rb, ldsB + s * GW_B + (wave * 24 + q * 8) * 128, vo, k0);
+  };
+  auto issue_a = [&](int kt) {
 #pragma unroll
-    for (int q = 0; q < GW_LB; ++q) {
-      const int ch = ((q + wave) & 1) ? ch_odd : ch_even;
-      uint32_t vo = rowB + uint32_t(q * 8) * uint32_t(p.ldb) + uint32_t(ch * 16);
-      if (!K_ALIGNED && int(k0) + ch * 16 >= K) vo = 0x80000000u;
-      dma_b128(rb, ldsB + s * GW_B + (wave * 24 + q * 8) * 128, vo, k0);
-    }
+    for (int q = 0; q < GW_LA; ++q) load_a(kt, q);
+  };
+  auto issue_b = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < GW_LB; ++q) load_b(kt, q);
+  };
+  // The loads that K step kt issues (A of kt + 1, then the weights of kt +
+  // 2), spread over its six column slots so that the load instructions queue
+  // between MFMAs instead of holding them back at the top of the step.
+  auto issue_slot = [&](int kt, int j) {
+    if (j == 0) { load_a(kt + 1, 0); load_a(kt + 1, 1); }
+    if (j == 1) { load_a(kt + 1, 2); load_a(kt + 1, 3); }
+    if (j == 2) load_a(kt + 1, 4);
+    if (j >= 3) load_b(kt + 2, j - 3);
   };
 
   // ---------------- registers ----------------
@@ -196,19 +214,26 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
 
-  // One K step with the wave's first NV row fragments (the rest are past
-  // the m-block's rows).  The weight fragment of column j + 1 is read while
-  // column j's MFMAs run.  Blockwise: each MFMA's 128-K partial is promoted
-  // into the accumulator one MFMA later (acc += P sA(row) sB(block)), so the
-  // FMAs never wait for the MFMA that produces their input.
-  auto compute = [&](auto nv_c, int kt) {
-    constexpr int NV = decltype(nv_c)::value;
+  // One K step.  The weight fragment of column j + 1 is read while column
+  // j's MFMAs run.  Rowwise: the fifth row fragment only where the m-block
+  // reaches it (an m-block of at most 256 rows has four per wave), and no
+  // column fragment past the n-block's columns (176 of 192 at N = 1408): a
+  // wave-uniform branch per column.  Blockwise: each MFMA's 128-K partial is
+  // promoted into the accumulator one MFMA later (acc += P sA(row)
+  // sB(block)), so the FMAs never wait for the MFMA that produces their
+  // input; that pipeline runs every fragment.  Every wave holds all five row
+  // fragments' accumulators: a form per count of valid fragments, or a
+  // branch per MFMA, makes the compiler keep more fragments live than the
+  // 256 registers hold.
+  auto compute = [&](int kt) {
+    constexpr int NV = GW_RF;
     const uint8_t* As = a_ring + (kt & 1) * GW_ASTAGE_PAD;
     const uint8_t* Bs = b_ring + (kt % 3) * GW_B;
     v8i a[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) a[i] = read_frag16(As, rg + 4 * i);
-    
+    for (int i = 0; i < NV; ++i)
+      if (BLOCKWISE || i < NV - 1 || five) a[i] = read_frag16(As, rg + 4 * i);
+
     [[maybe_unused]] float fa[NV];
     [[maybe_unused]] const float* sbs = reinterpret_cast<const float*>(As + GW_A + GW_SA);
     if constexpr (BLOCKWISE) {
@@ -221,32 +246,30 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
     v8i b = read_frag16(Bs, col_base / 16);
 #pragma unroll
     for (int j = 0; j < GW_CF; ++j) {
-      // column fragments past the n-block's columns (176 of 192 at N = 1408)
-      // are the last ones: stop there (rowwise; the blockwise promotion
-      // pipeline runs every fragment)
-      if (!BLOCKWISE && col_base + 16 * j >= cols_valid) break;
+      issue_slot(kt, j);
+      const bool col_j = BLOCKWISE || col_base + 16 * j < cols_valid;
       v8i bnext = b;
-      if (j + 1 < GW_CF) bnext = read_frag16(Bs, col_base / 16 + j + 1);
+      if (j + 1 < GW_CF && (BLOCKWISE || col_base + 16 * (j + 1) < cols_valid))
+        bnext = read_frag16(Bs, col_base / 16 + j + 1);
       [[maybe_unused]] float sbj = 0.f;
       if constexpr (BLOCKWISE) sbj = sbs[(n0 + col_base + 16 * j) / 128 - blk0];
+      if (col_j) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        // the fifth row fragment only where the m-block reaches it (an
-        // m-block of at most 256 rows has four per wave); one branch per
-        // column, on a wave-uniform condition
-        if (!BLOCKWISE && i == NV - 1 && !five) continue;
-        if constexpr (BLOCKWISE) {
-          const v4f t = mfma_16x16x128(b, a[i], v4f{0.f, 0.f, 0.f, 0.f});
-          if (i > 0 || j > 0) {
-            const int ip = i > 0 ? i - 1 : NV - 1;
-            const int jp = i > 0 ? j : j - 1;
+        for (int i = 0; i < NV; ++i) {
+          if (!BLOCKWISE && i == NV - 1 && !five) continue;
+          if constexpr (BLOCKWISE) {
+            const v4f t = mfma_16x16x128(b, a[i], v4f{0.f, 0.f, 0.f, 0.f});
+            if (i > 0 || j > 0) {
+              const int ip = i > 0 ? i - 1 : NV - 1;
+              const int jp = i > 0 ? j : j - 1;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[ip][jp][c] = __builtin_fmaf(t_prev[c], f_prev, acc[ip][jp][c]);
+              for (int c = 0; c < 4; ++c) acc[ip][jp][c] = __builtin_fmaf(t_prev[c], f_prev, acc[ip][jp][c]);
+            }
+            t_prev = t;
+            f_prev = fa[i] * sbj;
+          } else {
+            acc[i][j] = mfma_16x16x128(b, a[i], acc[i][j]);
           }
-          t_prev = t;
-          f_prev = fa[i] * sbj;
-        } else {
-          acc[i][j] = mfma_16x16x128(b, a[i], acc[i][j]);
         }
       }
       b = bnext;
@@ -259,14 +282,9 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
       for (int c = 0; c < 4; ++c) acc[NV - 1][GW_CF - 1][c] = __builtin_fmaf(t_prev[c], f_prev, acc[NV - 1][GW_CF - 1][c]);
     }
   };
-  // Every wave runs all five row fragments: row fragments past the
-  // m-block's rows multiply zeros (MFMA time only, no memory traffic).  A form
-  // per count of valid fragments, or a branch per MFMA, makes the compiler
-  // keep more fragments live than the 256 registers hold.
-  auto compute_nv = [&](int kt) { compute(std::integral_constant<int, GW_RF>{}, kt); };
 
   // ---------------- K loop ----------------
-  // Before step kt: A (and scales) of kt+1 go to A slot (kt+1) % 2 and the
+  // During step kt, A (and scales) of kt+1 go to A slot (kt+1) % 2 and the
   // weights of kt+2 to B slot (kt+2) % 3, both last read by step kt-1, which
   // every wave finished before the previous barrier.  After step kt each
   // wave waits for all but its newest three loads (the weights of kt+2), so
@@ -294,9 +312,12 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   for (int kt = 0; kt < nk; ++kt) {
-    issue_a(kt + 1);
-    issue_b(kt + 2);
-    if (cact) compute_nv(kt);
+    if (cact) {
+      compute(kt);
+    } else {
+#pragma unroll
+      for (int j = 0; j < GW_CF; ++j) issue_slot(kt, j);
+    }
     asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_barrier" ::: "memory");
