@@ -17,10 +17,25 @@
 namespace fp8mm {
 namespace grp {
 
+__device__ __forceinline__ int64_t clamp_offset(int32_t v, int64_t rows) {
+  const int64_t x = v < 0 ? 0 : int64_t(v);
+  return x > rows ? rows : x;
+}
+
+// Both offsets are loaded before either is used, so their latencies overlap.
 __device__ __forceinline__ void expert_range(const int32_t* offs, int64_t rows, int64_t e, int64_t& start,
                                              int64_t& end) {
-  end = min<int64_t>(max<int64_t>(offs[e], 0), rows);
-  start = e == 0 ? 0 : min<int64_t>(max<int64_t>(offs[e - 1], 0), rows);
+  const int32_t hi = offs[e];
+  const int32_t lo = offs[e > 0 ? e - 1 : 0];
+  end = clamp_offset(hi, rows);
+  start = e == 0 ? 0 : clamp_offset(lo, rows);
+}
+
+// A value every lane holds, in scalar registers (so that the code that
+// depends on it branches and addresses with scalar instructions).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  return int64_t((uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(v >> 32)))) << 32) |
+                 uint32_t(__builtin_amdgcn_readfirstlane(int(v))));
 }
 
 __device__ __forceinline__ int runs_of(int64_t start, int64_t end, int bm) {
@@ -33,11 +48,14 @@ __device__ inline bool find_run(const int32_t* offs, int64_t E, int64_t rows, in
                                 int64_t& row0, int64_t& row_end) {
   const int lane = threadIdx.x & 63;
   int base = 0;
+  int64_t carry = 0;    // clamped end offset of expert e0 - 1
   for (int64_t e0 = 0; e0 < E; e0 += 64) {
     const int64_t e = e0 + lane;
-    int64_t start = 0, end = 0;
-    if (e < E) expert_range(offs, rows, e, start, end);
-    const int cnt = runs_of(start, end, bm);
+    // one offset per lane; an expert's start is the previous lane's end
+    const int64_t end = e < E ? clamp_offset(offs[e], rows) : 0;
+    const int64_t prev = __shfl_up(end, 1, 64);
+    const int64_t start = lane == 0 ? carry : prev;
+    const int cnt = e < E ? runs_of(start, end, bm) : 0;
     int incl = cnt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -49,12 +67,14 @@ __device__ inline bool find_run(const int32_t* offs, int64_t E, int64_t rows, in
     if (mask) {
       const int src = __builtin_ctzll(mask);
       const int excl = __shfl(incl - cnt, src, 64);
-      e_out = int(e0) + src;
-      row0 = __shfl(start, src, 64) + int64_t(g - base - excl) * bm;
-      row_end = __shfl(end, src, 64);
+      // in scalar registers: the tile's addressing and branches depend on them
+      e_out = __builtin_amdgcn_readfirstlane(int(e0) + src);
+      row0 = uniform64(__shfl(start, src, 64) + int64_t(g - base - excl) * bm);
+      row_end = uniform64(__shfl(end, src, 64));
       return true;
     }
     base += __shfl(incl, 63, 64);
+    carry = __shfl(end, 63, 64);
   }
   return false;
 }
@@ -112,9 +132,9 @@ __device__ inline bool find_mtile_long_first(const int32_t* offs, int64_t E, int
     if (mask) {
       const int src = __builtin_ctzll(mask);
       const int excl = __shfl(incl - cnt, src, 64);
-      e_out = int(e0) + src;
-      const int64_t s = __shfl(start, src, 64);
-      const int64_t en = __shfl(end, src, 64);
+      e_out = __builtin_amdgcn_readfirstlane(int(e0) + src);
+      const int64_t s = uniform64(__shfl(start, src, 64));
+      const int64_t en = uniform64(__shfl(end, src, 64));
       // a long tile j starts at 256 j; the short tile after the full ones
       row0 = want_long ? s + int64_t(gg - base - excl) * BM : s + (en - s) / BM * BM;
       row_end = en;
@@ -141,11 +161,10 @@ __device__ inline void runs_before(const int32_t* offs, int64_t rows, int bm, in
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
   // every lane holds the sum: make it visibly wave-uniform (scalar registers)
-  first = int64_t((uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(acc >> 32)))) << 32) |
-                  uint32_t(__builtin_amdgcn_readfirstlane(int(acc))));
+  first = uniform64(acc);
   int64_t start, end;
   expert_range(offs, rows, e, start, end);
-  count = runs_of(start, end, bm);
+  count = __builtin_amdgcn_readfirstlane(runs_of(start, end, bm));
 }
 
 }  // namespace grp
