@@ -79,6 +79,37 @@ def test_grouped_blockwise(E, N, K, sizes, layout):
     _assert_close(got, ref, f"grouped 1x128 x 128x128 E={E} N={N} K={K} {layout}")
 
 
+def _many_experts_sizes():
+    """150 experts (three 64-expert chunks of the offset scan): empty experts
+    on both sides of the first chunk boundary, one of 700 rows (three
+    320-row m-blocks) just before the second and a single row just after."""
+    sizes = workloads.streams(150, 1)[0].integers(0, 300, size=150)
+    sizes[[63, 64]] = 0
+    sizes[127], sizes[128] = 700, 1
+    return sizes
+
+
+@pytest.mark.parametrize("layout", ["NK", "KN"])
+def test_grouped_blockwise_more_than_64_experts(layout):
+    """The offset scans carry from one chunk of 64 experts to the next: E =
+    150 on the weight-streaming kernel (weights read [N, K]) and on the
+    streaming kernel (read [K, N]), and E = 70 experts of 400-900 rows on the
+    streaming kernel's long-tiles-first order."""
+    got, ref = _grouped_blockwise_case(150, 256, 256, _many_experts_sizes(), layout, seed=151)
+    _assert_close(got, ref, f"grouped blockwise E=150 {layout}")
+    sizes = workloads.streams(70, 1)[0].integers(400, 900, size=70)
+    got, ref = _grouped_blockwise_case(70, 256, 256, sizes, layout, seed=71)
+    _assert_close(got, ref, f"grouped blockwise E=70, long experts, {layout}")
+
+
+def test_grouped_weight_gradient_more_than_64_experts():
+    sizes = _many_experts_sizes()
+    got, ref = _grouped_grad_weight_case(sizes, 128, 256, seed=152, out_dtype=torch.float32)
+    for e in np.flatnonzero(sizes == 0):
+        assert not got[e].any(), "an expert without tokens gets zeros"
+    _assert_close(got, ref, "grouped grad_weight E=150", out_dtype="fp32")
+
+
 @pytest.mark.parametrize("bias_form", ["shared", "per_expert"])
 @pytest.mark.parametrize("layout", ["NK", "KN"])
 def test_grouped_blockwise_bias_fp32(layout, bias_form):
