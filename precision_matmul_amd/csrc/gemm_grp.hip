@@ -393,8 +393,32 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
     // copy-out: staged rows [0, rows_valid), the pass's valid columns
     const int pc0 = pass * PW;                              // first tile column of the pass
     const int pcols = min(PW, cols_valid - pc0);            // valid columns in the pass
-    if (pcols > 0) {
-      const int cpr = (pcols * OUTB + 15) / 16;
+    const int cpr = (pcols * OUTB + 15) / 16;
+    if (pcols > 0 && vec_out && (pcols * OUTB) % 16 == 0) {
+      // whole 16-byte chunks only: each thread has four LDS reads in flight
+      // before their stores (one at a time, every copy waited out the LDS
+      // latency)
+      constexpr int NT = GW_NW * 64;
+      const int total = rows_valid * CPR_MAX;
+      uint8_t* const obase = reinterpret_cast<uint8_t*>(p.out) + (row0 * p.ldo + n0 + pc0) * OUTB;
+      for (int base = int(threadIdx.x); base < total; base += 4 * NT) {
+        v4i val[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = base + u * NT;
+          const int rt = idx / CPR_MAX, ch = idx % CPR_MAX;
+          if (idx < total && ch < cpr) val[u] = *reinterpret_cast<const v4i*>(smem + rt * PITCH + ch * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = base + u * NT;
+          const int rt = idx / CPR_MAX, ch = idx % CPR_MAX;
+          // plain stores: L2 merges the partial lines at the n-block edges
+          // (non-temporal ones wrote 51 MB for the 46 MB MoE output)
+          if (idx < total && ch < cpr) *reinterpret_cast<v4i*>(obase + int64_t(rt) * p.ldo * OUTB + ch * 16) = val[u];
+        }
+      }
+    } else if (pcols > 0) {
       for (int idx = int(threadIdx.x); idx < rows_valid * CPR_MAX; idx += GW_NW * 64) {
         const int rt = idx / CPR_MAX;
         const int ch = idx % CPR_MAX;
@@ -403,8 +427,6 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
         uint8_t* dst = reinterpret_cast<uint8_t*>(p.out) + ((row0 + rt) * p.ldo + n0 + pc0) * OUTB + ch * 16;
         const int nvals = min(16 / OUTB, pcols - ch * (16 / OUTB));
         if (vec_out && nvals == 16 / OUTB) {
-          // plain stores: L2 merges the partial lines at the n-block edges
-          // (non-temporal ones wrote 51 MB for the 46 MB MoE output)
           *reinterpret_cast<v4i*>(dst) = *reinterpret_cast<const v4i*>(src);
         } else {
           for (int e2 = 0; e2 < nvals; ++e2) {
