@@ -534,6 +534,33 @@ __global__ __launch_bounds__(WM * WN * 64, GROUPED_K ? 2 : 1) void gemm_kernel(G
     __syncthreads();
     constexpr int CPR = EPI_COLS * OUTB / 16;       // 16-byte chunks per staged row
     constexpr int EPR = 16 / OUTB;                  // elements per chunk
+    constexpr int ITER = TM * CPR / 64;             // 16-byte copies per lane and pass
+    constexpr int BATCH = ITER % 4 == 0 ? 4 : (ITER % 2 == 0 ? 2 : 1);
+    static_assert((TM * CPR) % 64 == 0, "copy-out per lane");
+    if (vec_out && row_base + TM <= ti.rows_valid && col_base + TN <= ti.cols_valid) {
+      // The wave's whole sub-tile is inside the output: no per-chunk
+      // conditions, so each lane has BATCH LDS reads in flight before their
+      // stores (one at a time, every copy waited out the LDS latency).
+      uint8_t* const obase = reinterpret_cast<uint8_t*>(p.out) +
+                             ((ti.out_off + int64_t(blockIdx.y) * p.split_stride +
+                               (ti.row0 - p.out_row0 + row_base) * p.ldo + ti.n0 + col_base + pass * EPI_COLS) * OUTB);
+#pragma unroll
+      for (int u0 = 0; u0 < ITER; u0 += BATCH) {
+        v4i val[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int idx = lane + (u0 + u) * 64;
+          val[u] = *reinterpret_cast<const v4i*>(ep + (idx / CPR) * EPI_PITCH + (idx % CPR) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int idx = lane + (u0 + u) * 64;
+          *reinterpret_cast<v4i*>(obase + int64_t(idx / CPR) * p.ldo * OUTB + (idx % CPR) * 16) = val[u];
+        }
+      }
+      if (pass + 1 < EPI_PASSES) __syncthreads();
+      continue;
+    }
 #pragma unroll 4
     for (int idx = lane; idx < TM * CPR; idx += 64) {
       const int rl = idx / CPR;

@@ -783,6 +783,35 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     __syncthreads();
     constexpr int CPR = EPI_COLS * OUTB / 16;
     constexpr int EPR = 16 / OUTB;
+    constexpr int ITER = SY_TM * CPR / 64;    // 16-byte copies per lane and pass
+    static_assert(ITER % 4 == 0, "copy-out batches");
+    if (vec_out && row_base + SY_TM <= rows_valid && col_base + SY_TN <= cols_valid) {
+      // The wave's whole sub-tile is inside the output: no per-chunk
+      // conditions, so each lane has four LDS reads in flight before their
+      // stores (one at a time, every copy waited out the LDS latency).
+      uint8_t* const obase = reinterpret_cast<uint8_t*>(p.out) +
+                             (out_off + (row0 + row_base) * p.ldo + n0 + col_base + pass * EPI_COLS) * OUTB;
+#pragma unroll
+      for (int u0 = 0; u0 < ITER; u0 += 4) {
+        v4i val[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = lane + (u0 + u) * 64;
+          val[u] = *reinterpret_cast<const v4i*>(ep + (idx / CPR) * EPI_PITCH + (idx % CPR) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = lane + (u0 + u) * 64;
+          uint8_t* dst = obase + int64_t(idx / CPR) * p.ldo * OUTB + (idx % CPR) * 16;
+          if constexpr (GROUPED || GROUPED_K)
+            __builtin_nontemporal_store(val[u], reinterpret_cast<v4i*>(dst));
+          else
+            *reinterpret_cast<v4i*>(dst) = val[u];
+        }
+      }
+      if (pass + 1 < EPI_PASSES) __syncthreads();
+      continue;
+    }
 #pragma unroll 4
     for (int idx = lane; idx < SY_TM * CPR; idx += 64) {
       const int rl = idx / CPR;
