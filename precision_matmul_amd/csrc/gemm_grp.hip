@@ -221,12 +221,15 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
   // wave-uniform branch per column.  Blockwise: each MFMA's 128-K partial is
   // promoted into the accumulator one MFMA later (acc += P sA(row)
   // sB(block)), so the FMAs never wait for the MFMA that produces their
-  // input; that pipeline runs every fragment.  Every wave holds all five row
-  // fragments' accumulators: a form per count of valid fragments, or a
-  // branch per MFMA, makes the compiler keep more fragments live than the
-  // 256 registers hold.
-  auto compute = [&](int kt) {
+  // input; that pipeline runs every row fragment and NC column fragments (a
+  // last column wholly past the n-block, as in the second column group at
+  // bn = 176, is left out: a form of the step per column count).  Every wave
+  // holds all five row fragments' accumulators: a form per count of valid
+  // row fragments, or a branch per MFMA, makes the compiler keep more
+  // fragments live than the 256 registers hold.
+  auto compute = [&](int kt, auto nc) {
     constexpr int NV = GW_RF;
+    constexpr int NC = BLOCKWISE ? decltype(nc)::value : GW_CF;
     const uint8_t* As = a_ring + (kt & 1) * GW_ASTAGE_PAD;
     const uint8_t* Bs = b_ring + (kt % 3) * GW_B;
     v8i a[NV];
@@ -247,9 +250,9 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
 #pragma unroll
     for (int j = 0; j < GW_CF; ++j) {
       issue_slot(kt, j);
-      const bool col_j = BLOCKWISE || col_base + 16 * j < cols_valid;
+      const bool col_j = BLOCKWISE ? j < NC : col_base + 16 * j < cols_valid;
       v8i bnext = b;
-      if (j + 1 < GW_CF && (BLOCKWISE || col_base + 16 * (j + 1) < cols_valid))
+      if (j + 1 < GW_CF && (BLOCKWISE ? j + 1 < NC : col_base + 16 * (j + 1) < cols_valid))
         bnext = read_frag16(Bs, col_base / 16 + j + 1);
       [[maybe_unused]] float sbj = 0.f;
       if constexpr (BLOCKWISE) sbj = sbs[(n0 + col_base + 16 * j) / 128 - blk0];
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
     }
     if constexpr (BLOCKWISE) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[NV - 1][GW_CF - 1][c] = __builtin_fmaf(t_prev[c], f_prev, acc[NV - 1][GW_CF - 1][c]);
+      for (int c = 0; c < 4; ++c) acc[NV - 1][NC - 1][c] = __builtin_fmaf(t_prev[c], f_prev, acc[NV - 1][NC - 1][c]);
     }
   };
 
@@ -311,18 +314,25 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (cact) {
-      compute(kt);
-    } else {
+  auto k_loop = [&](auto nc) {
+    for (int kt = 0; kt < nk; ++kt) {
+      if (cact) {
+        compute(kt, nc);
+      } else {
 #pragma unroll
-      for (int j = 0; j < GW_CF; ++j) issue_slot(kt, j);
+        for (int j = 0; j < GW_CF; ++j) issue_slot(kt, j);
+      }
+      asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  };
+  // blockwise: the last column fragment only where it holds any of the n-block's columns
+  if (!BLOCKWISE || col_base + 16 * (GW_CF - 1) < cols_valid)
+    k_loop(std::integral_constant<int, GW_CF>());
+  else
+    k_loop(std::integral_constant<int, GW_CF - 1>());
   // the dead loads of the last two steps (zeros into unread slots)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
