@@ -221,14 +221,16 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
   // wave-uniform branch per column.  Blockwise: each MFMA's 128-K partial is
   // promoted into the accumulator one MFMA later (acc += P sA(row)
   // sB(block)), so the FMAs never wait for the MFMA that produces their
-  // input; that pipeline runs every row fragment and NC column fragments (a
-  // last column wholly past the n-block, as in the second column group at
-  // bn = 176, is left out: a form of the step per column count).  Every wave
-  // holds all five row fragments' accumulators: a form per count of valid
-  // row fragments, or a branch per MFMA, makes the compiler keep more
-  // fragments live than the 256 registers hold.
-  auto compute = [&](int kt, auto nc) {
-    constexpr int NV = GW_RF;
+  // input; that pipeline runs NV row and NC column fragments: a fifth row
+  // fragment past the m-block (every wave's, for an m-block of at most 256
+  // rows) and a last column wholly past the n-block (the second column
+  // group's at bn = 176) are left out, with one form of the K loop per
+  // count.  Every wave holds all five row fragments' accumulators either
+  // way: a branch per MFMA, or accumulators only for the fragments a form
+  // runs, makes the compiler keep more fragments live than the 256 registers
+  // hold.
+  auto compute = [&](int kt, auto nv, auto nc) {
+    constexpr int NV = BLOCKWISE ? decltype(nv)::value : GW_RF;
     constexpr int NC = BLOCKWISE ? decltype(nc)::value : GW_CF;
     const uint8_t* As = a_ring + (kt & 1) * GW_ASTAGE_PAD;
     const uint8_t* Bs = b_ring + (kt % 3) * GW_B;
@@ -314,10 +316,10 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  auto k_loop = [&](auto nc) {
+  auto k_loop = [&](auto nv, auto nc) {
     for (int kt = 0; kt < nk; ++kt) {
       if (cact) {
-        compute(kt, nc);
+        compute(kt, nv, nc);
       } else {
 #pragma unroll
         for (int j = 0; j < GW_CF; ++j) issue_slot(kt, j);
@@ -328,11 +330,21 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // blockwise: the last column fragment only where it holds any of the n-block's columns
-  if (!BLOCKWISE || col_base + 16 * (GW_CF - 1) < cols_valid)
-    k_loop(std::integral_constant<int, GW_CF>());
+  // blockwise: the fifth row fragment and the last column fragment only
+  // where they hold any of the tile's rows or columns
+  using all_rows = std::integral_constant<int, GW_RF>;
+  using all_cols = std::integral_constant<int, GW_CF>;
+  using four_rows = std::integral_constant<int, GW_RF - 1>;
+  using five_cols = std::integral_constant<int, GW_CF - 1>;
+  const bool six = col_base + 16 * (GW_CF - 1) < cols_valid;
+  if (!BLOCKWISE || (five && six))
+    k_loop(all_rows(), all_cols());
+  else if (five)
+    k_loop(all_rows(), five_cols());
+  else if (six)
+    k_loop(four_rows(), all_cols());
   else
-    k_loop(std::integral_constant<int, GW_CF - 1>());
+    k_loop(four_rows(), five_cols());
   // the dead loads of the last two steps (zeros into unread slots)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
