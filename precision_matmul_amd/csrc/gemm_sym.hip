@@ -325,11 +325,13 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
 
   // ---------------- registers ----------------
   // Wave w < 4 takes rows [64 w, +64) of columns [0, 128); wave w >= 4 rows
-  // [64 ((w + 1) & 3), +64) of columns [128, 256).  The SIMD of wave w is
+  // [64 ((w + 2) & 3), +64) of columns [128, 256).  The SIMD of wave w is
   // w % 4, so the two waves of a SIMD share neither rows nor columns: a tile
-  // with only its first 64 rows valid keeps two SIMDs busy (waves 0 and 7),
-  // one with only its first 128 columns valid all four (waves 0-3).
-  const int wm = wave < 4 ? wave : (wave + 1) & 3;
+  // with only its first 64 rows valid keeps two SIMDs busy (waves 0 and 6),
+  // one with only its first 128 rows valid all four with one wave each
+  // (waves 0, 1, 6, 7), one with only its first 128 columns valid all four
+  // (waves 0-3).
+  const int wm = wave < 4 ? wave : (wave + 2) & 3;
   const int wn = wave >> 2;
   const int row_base = wm * SY_TM;               // sub-tile origin within the tile
   const int col_base = wn * SY_TN;
