@@ -88,12 +88,11 @@ template <Epi EPI, bool OUT_BF16, bool BIAS, bool K_ALIGNED, bool B_KN, bool GRO
 __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                                    int vec_out) {
   constexpr bool BLOCKWISE = EPI == Epi::Block128x128 || EPI == Epi::Block128x1;
-  // Operand order of the MFMA.  SWAP computes each 16 x 16 output block
+  // Operand order of the MFMA: each 16 x 16 output block is computed
   // transposed (B fragment as the instruction's first operand), so a lane
   // holds one output row and four adjacent columns: one promotion factor per
-  // lane and row fragment for a 128x128 B.  A 128x1 B scales columns, so it
-  // keeps the plain order (one output column and four rows per lane).
-  constexpr bool SWAP = EPI != Epi::Block128x1;
+  // lane and row fragment for a 128x128 B, and one row factor times four
+  // column factors for a 128x1 B.
   // MXFP8: the MFMA applies the E8M0 byte of lane group g (for the lane's
   // row or column) to K [32 g, 32 g + 32) of the step, i.e. to chunks 2g and
   // 2g + 1, in the fragment order below.
@@ -101,7 +100,8 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   static_assert(!MX || (!B_KN && !GROUPED), "MXFP8: plain GEMMs with B stored [N, K]");
   static_assert(!GROUPED || EPI == Epi::Row || EPI == Epi::Block128x128, "grouped: rowwise or 1x128 x 128x128");
   static_assert(!GROUPED_K || (EPI == Epi::Block128x1 && !B_KN && !GROUPED && !BIAS), "grouped weight gradient");
-  using Fac = std::conditional_t<SWAP, float, v4f>;
+  // promotion factor of one MFMA result: per lane (128x128) or per element (128x1)
+  using Fac = std::conditional_t<EPI == Epi::Block128x1, v4f, float>;
   constexpr int OUTB = OUT_BF16 ? 2 : 4;
   constexpr int EPI_PASSES = epi_passes(SY_NW, SY_TM, SY_TN, OUTB, SY_STAGE);
   constexpr int EPI_COLS = SY_TN / EPI_PASSES;
@@ -374,23 +374,23 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
     else return read_frag(tile, nc + frow);
   };
   auto stage_ptr = [&](int s) -> const uint8_t* { return s == 0 ? stage0 : stage1; };
-  // Blockwise: per-lane scales of the 4 row fragments (sA of the lane's 4
-  // rows) and the B scales (128x128: the block scale, folded into the row
-  // factors in column 0 of the step that uses them; 128x1: one per column).
-  auto read_fa = [&](const uint8_t* st, Fac* fa_out, float* sbv_out) {
+  // Blockwise: per-lane scales of the 4 row fragments (sA of the lane's row
+  // in each) and, for 128x128, the B block scale (folded into the row
+  // factors in column 0 of the step that uses them).
+  auto read_fa = [&](const uint8_t* st, float* fa_out, float* sbv_out) {
     const float* sas = reinterpret_cast<const float*>(st + SY_A + SY_B);
     const float* sbs = sas + SY_SCALE / 4;
 #pragma unroll
     for (int i = 0; i < SY_FM; ++i) {
-      if constexpr (SWAP) fa_out[i] = sas[row_base + i * 16 + frow];
-      else fa_out[i] = *reinterpret_cast<const v4f*>(sas + row_base + i * 16 + fq * 4);
+      fa_out[i] = sas[row_base + i * 16 + frow];
     }
-    if constexpr (EPI == Epi::Block128x128) {
-      sbv_out[0] = sbs[(col_base / 128) * 64];
-    } else if constexpr (EPI == Epi::Block128x1) {
-#pragma unroll
-      for (int j = 0; j < SY_FN; ++j) sbv_out[j] = sbs[col_base + j * 16 + frow];
-    }
+    if constexpr (EPI == Epi::Block128x128) sbv_out[0] = sbs[(col_base / 128) * 64];
+  };
+  // 128x1: the four column factors of the lane's columns in fragment column
+  // j of a stage
+  [[maybe_unused]] auto read_colf = [&](const uint8_t* st, int j) {
+    const float* sbs = reinterpret_cast<const float*>(st + SY_A + SY_B) + SY_SCALE / 4;
+    return *reinterpret_cast<const v4f*>(sbs + col_base + j * 16 + fq * 4);
   };
 
   v8i a[SY_FM];
@@ -402,13 +402,14 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   [[maybe_unused]] auto mx_byte = [&](const uint8_t* stage, int region, int idx) {
     return int(stage[SY_A + SY_B + region + idx * 4 + fq]);
   };
-  // Promotion factors of the current / next step.  128x1 keeps one set: the
-  // next step's value of each replaces the current one right after its last
-  // use in column 7 (the registers its per-column scales need do not allow
-  // two sets).
+  // Promotion factors of the current / next step.  128x1 keeps one set of
+  // row factors: the next step's value of each replaces the current one
+  // right after its last use in column 7; its column factors are read one
+  // fragment column ahead into a ring of two (colf).
   constexpr int FSETS = EPI == Epi::Block128x1 ? 1 : 2;
-  [[maybe_unused]] Fac fa[FSETS][SY_FM];
-  [[maybe_unused]] float sbv[FSETS][SY_FN];
+  [[maybe_unused]] float fa[FSETS][SY_FM];
+  [[maybe_unused]] float sbv[FSETS][1];
+  [[maybe_unused]] v4f colf[2];
   // Blockwise promotion runs two MFMAs behind: pending results and where they go.
   [[maybe_unused]] v4f pend_t[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
   [[maybe_unused]] Fac pend_f[2] = {Fac{}, Fac{}};
@@ -444,10 +445,9 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
           // eight B fragments live (and spilling).
           asm volatile("" : "+v"(acc[i][j]));
         } else if constexpr (!BLOCKWISE) {
-          acc[i][j] = SWAP ? mfma_16x16x128(bf, a[i], acc[i][j]) : mfma_16x16x128(a[i], bf, acc[i][j]);
+          acc[i][j] = mfma_16x16x128(bf, a[i], acc[i][j]);
         } else {
-          const v4f t = SWAP ? mfma_16x16x128(bf, a[i], v4f{0.f, 0.f, 0.f, 0.f})
-                             : mfma_16x16x128(a[i], bf, v4f{0.f, 0.f, 0.f, 0.f});
+          const v4f t = mfma_16x16x128(bf, a[i], v4f{0.f, 0.f, 0.f, 0.f});
           // promote the result of slot m - 2 (possibly of the previous step)
           {
             const int mp = m - 2;
@@ -461,9 +461,9 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
           if constexpr (EPI == Epi::Block128x128) {
             if (j == 0) fa[F % FSETS][i] = fa[F % FSETS][i] * sbv[F % FSETS][0];
             pend_f[m & 1] = fa[F % FSETS][i];
-          } else if constexpr (!SWAP) {
+          } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pend_f[m & 1][e] = fa[F % FSETS][i][e] * sbv[F % FSETS][j];
+            for (int e = 0; e < 4; ++e) pend_f[m & 1][e] = fa[F % FSETS][i] * colf[j & 1][e];
           }
         }
         if constexpr (BLOCKWISE) {
@@ -477,9 +477,11 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
           if (j + 1 < SY_FN) {
             bring[(j + 1) & 1] = read_b(Bs, col_base + (j + 1) * 16);
             if constexpr (MX) mxb[(j + 1) & 1] = mx_byte(As, SY_SCALE, col_base + (j + 1) * 16 + frow);
+            if constexpr (EPI == Epi::Block128x1) colf[(j + 1) & 1] = read_colf(As, j + 1);
           } else {
             bring[0] = read_b(An + SY_A, col_base);
             if constexpr (MX) mxb[0] = mx_byte(An, SY_SCALE, col_base + frow);
+            if constexpr (EPI == Epi::Block128x1) colf[0] = read_colf(An, 0);
           }
         }
         // next step's A fragment i, right after its last use
@@ -492,16 +494,8 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
           if constexpr (FSETS == 2) {
             if (j == SY_FN - 1 && i == 1) read_fa(An, fa[F ^ 1], sbv[F ^ 1]);
           } else if (j == SY_FN - 1) {
-            // 128x1, one set: row factors i after their last use (slot 7, i);
-            // column scales 0..6 in slot (7, 0), column 7 after slot (7, 3)
-            const float* sas_n = reinterpret_cast<const float*>(An + SY_A + SY_B);
-            const float* sbs_n = sas_n + SY_SCALE / 4;
-            if constexpr (!SWAP) fa[0][i] = *reinterpret_cast<const v4f*>(sas_n + row_base + i * 16 + fq * 4);
-            if (i == 0) {
-#pragma unroll
-              for (int jj = 0; jj < SY_FN - 1; ++jj) sbv[0][jj] = sbs_n[col_base + jj * 16 + frow];
-            }
-            if (i == SY_FM - 1) sbv[0][SY_FN - 1] = sbs_n[col_base + (SY_FN - 1) * 16 + frow];
+            // 128x1, one set: row factor i after its last use (slot 7, i)
+            fa[0][i] = reinterpret_cast<const float*>(An + SY_A + SY_B)[row_base + i * 16 + frow];
           }
         }
         // loads: A of step kt+2 into this stage (free after the barrier) in
@@ -648,6 +642,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       for (int i = 0; i < SY_FM; ++i) a[i] = read_frag(stage0, row_base + i * 16 + frow);
       bring[0] = read_b(stage0 + SY_A, col_base);
       if constexpr (BLOCKWISE) read_fa(stage0, fa[0], sbv[0]);
+      if constexpr (EPI == Epi::Block128x1) colf[0] = read_colf(stage0, 0);
       if constexpr (MX) {
 #pragma unroll
         for (int i = 0; i < SY_FM; ++i) mxa[i] = mx_byte(stage0, 0, row_base + i * 16 + frow);
@@ -692,30 +687,26 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
   // latency overlaps the wait for the last loads and each other.
   [[maybe_unused]] float s_tensor = 0.f;
   if constexpr (EPI == Epi::Tensor) s_tensor = p.sa[0] * p.sb[0];
-  // Row scales of the lane's rows: SWAP, one row per row fragment (i * 16 +
-  // frow); otherwise four (i * 16 + 4 fq + e).
-  [[maybe_unused]] float sar[SY_FM][4];
+  // Row scale of the lane's row in each row fragment (i * 16 + frow).
+  [[maybe_unused]] float sar[SY_FM];
   if constexpr (EPI == Epi::Row) {
 #pragma unroll
-    for (int i = 0; i < SY_FM; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rt = row_base + i * 16 + (SWAP ? frow : fq * 4 + e);
-        sar[i][e] = (SWAP && e > 0) ? sar[i][0] : (rt < rows_valid ? p.sa[row0 + rt] : 0.f);
-      }
+    for (int i = 0; i < SY_FM; ++i) {
+      const int rt = row_base + i * 16 + frow;
+      sar[i] = rt < rows_valid ? p.sa[row0 + rt] : 0.f;
+    }
   }
-  // Column scales and bias of the lane's output columns: SWAP, four adjacent
-  // per column fragment j (4 fq + e); otherwise one (frow).
-  // With SWAP the four are contiguous: one 16-byte scale load and one 8-byte
-  // bias load per column fragment where alignment and the N edge allow.
+  // Column scales and bias of the lane's four adjacent output columns per
+  // column fragment j (4 fq + e): one 16-byte scale load and one 8-byte bias
+  // load per column fragment where alignment and the N edge allow.
   [[maybe_unused]] float sbc[SY_FN][4];
   [[maybe_unused]] float bias_v[SY_FN][4];
-  [[maybe_unused]] const bool sb_vec = SWAP && (reinterpret_cast<uintptr_t>(sbg) & 15) == 0;
-  [[maybe_unused]] const bool bias_vec = SWAP && (reinterpret_cast<uintptr_t>(biasg) & 7) == 0;
+  [[maybe_unused]] const bool sb_vec = (reinterpret_cast<uintptr_t>(sbg) & 15) == 0;
+  [[maybe_unused]] const bool bias_vec = (reinterpret_cast<uintptr_t>(biasg) & 7) == 0;
 #pragma unroll
   for (int j = 0; j < SY_FN; ++j) {
-    const int c0 = col_base + j * 16 + (SWAP ? fq * 4 : frow);
-    const bool whole = SWAP && c0 + 4 <= cols_valid;
+    const int c0 = col_base + j * 16 + fq * 4;
+    const bool whole = c0 + 4 <= cols_valid;
     if constexpr (EPI == Epi::Row) {
       if (sb_vec && whole) {
         const v4f t = *reinterpret_cast<const v4f*>(sbg + n0 + c0);
@@ -723,7 +714,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
         for (int e = 0; e < 4; ++e) sbc[j][e] = t[e];
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sbc[j][e] = (c0 + e < cols_valid && (SWAP || e == 0)) ? sbg[n0 + c0 + e] : 0.f;
+        for (int e = 0; e < 4; ++e) sbc[j][e] = c0 + e < cols_valid ? sbg[n0 + c0 + e] : 0.f;
       }
     }
     if constexpr (BIAS) {
@@ -736,8 +727,7 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          bias_v[j][e] = (c0 + e < cols_valid && (SWAP || e == 0))
-                             ? __uint_as_float(uint32_t(biasg[n0 + c0 + e]) << 16) : 0.f;
+          bias_v[j][e] = c0 + e < cols_valid ? __uint_as_float(uint32_t(biasg[n0 + c0 + e]) << 16) : 0.f;
       }
     }
   }
@@ -755,30 +745,18 @@ __global__ __launch_bounds__(SY_NW * 64, 1) void gemm_sym_kernel(GemmProblem p, 
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int ce = SWAP ? e : 0;
           v[e] = acc[i][j][e];
           if constexpr (EPI == Epi::Tensor) v[e] = v[e] * s_tensor;
-          if constexpr (EPI == Epi::Row) v[e] = (v[e] * sar[i][e]) * sbc[j][ce];
-          if constexpr (BIAS) v[e] = v[e] + bias_v[j][ce];
+          if constexpr (EPI == Epi::Row) v[e] = (v[e] * sar[i]) * sbc[j][e];
+          if constexpr (BIAS) v[e] = v[e] + bias_v[j][e];
         }
-        if constexpr (SWAP) {
-          uint8_t* dst = ep + (i * 16 + frow) * EPI_PITCH + (jj * 16 + fq * 4) * OUTB;
-          if constexpr (OUT_BF16) {
-            const uint32_t lo = uint32_t(f32_to_bf16_rne(v[0])) | (uint32_t(f32_to_bf16_rne(v[1])) << 16);
-            const uint32_t hi = uint32_t(f32_to_bf16_rne(v[2])) | (uint32_t(f32_to_bf16_rne(v[3])) << 16);
-            *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
-          } else {
-            *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
-          }
+        uint8_t* dst = ep + (i * 16 + frow) * EPI_PITCH + (jj * 16 + fq * 4) * OUTB;
+        if constexpr (OUT_BF16) {
+          const uint32_t lo = uint32_t(f32_to_bf16_rne(v[0])) | (uint32_t(f32_to_bf16_rne(v[1])) << 16);
+          const uint32_t hi = uint32_t(f32_to_bf16_rne(v[2])) | (uint32_t(f32_to_bf16_rne(v[3])) << 16);
+          *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
         } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            uint8_t* dst = ep + (i * 16 + fq * 4 + e) * EPI_PITCH + (jj * 16 + frow) * OUTB;
-            if constexpr (OUT_BF16)
-              *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16_rne(v[e]);
-            else
-              *reinterpret_cast<float*>(dst) = v[e];
-          }
+          *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
         }
       }
     }
