@@ -201,9 +201,11 @@ def test_split_tail_three_uneven_k_ranges(recipe):
     the streaming kernel takes the 12 tile rows that fill whole rounds (240
     tiles, rows 0 .. 3071) and the 228 remaining rows (20 tiles of 256 x 256,
     80 of 128 x 128) are split into min(256 / 80, 25 / 8, 8) = 3 K ranges of
-    8, 8 and 9 steps over the contraction of 3200 (25 steps of 128).  The same
-    split happens at 16640 x 5120 x 8192 (21 / 21 / 22 of 64 steps).  Every
-    element is compared; the rowwise case adds the bias in the reduction."""
+    8, 8 and 9 steps over the contraction of 3200 (25 steps of 128); with B
+    stored [K, N] (grad_input) the tail runs 40 tiles of 256 x 128 in
+    min(256 / 40, 25 / 8, 8) = 3 ranges.  The same split happens at 16640 x
+    5120 x 8192 (21 / 21 / 22 of 64 steps).  Every element is compared; the
+    rowwise case adds the bias in the reduction."""
     M, N, K = 3300, 5120, 3200
     if recipe == "grad_input":
         # grad_input [M, 5120] = grad_output [M, 3200] @ weight [3200, 5120] (B stored [K, N])
