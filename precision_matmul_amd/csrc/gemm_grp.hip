@@ -27,10 +27,13 @@
 //  * The n-blocks of one m-block run on one XCD, whose L2 then holds the
 //    m-block's A rows; m-blocks are dealt to the XCDs round-robin.
 //
-// Waves.  8 waves, wave w: row group rg = w & 3, column group cg = w >> 2.
-// Row fragment i (i < 5) of the wave is tile rows 16 (rg + 4 i) .. +15, so
-// the valid rows of a short m-block spread over all four SIMDs (SIMD = w &
-// 3); column fragment j (j < 6) is tile columns 96 cg + 16 j .. +15.  Each
+// Waves.  8 waves, wave w: column group cg = w >> 2, row group rg = (w +
+// cg) & 3.  Row fragment i (i < 5) of the wave is tile rows 16 (rg + 4 i) ..
+// +15, so the valid rows of a short m-block spread over all four SIMDs (SIMD
+// = w & 3), and the two waves of a SIMD have different row groups: a fifth
+// row fragment that only one row group has (an m-block of 257 to 272 rows)
+// falls on two SIMDs, not twice on one.  Column fragment j (j < 6) is tile
+// columns 96 cg + 16 j .. +15.  Each
 // fragment is a v_mfma_f32_16x16x128_f8f6f4 block computed transposed (the
 // weight fragment as the first operand), so a lane holds one output row and
 // four adjacent columns: one row scale per lane and fragment, 8- or 16-byte
@@ -188,8 +191,8 @@ __global__ __launch_bounds__(GW_NW * 64, 1) void gemm_grouped_wide_kernel(GemmPr
   };
 
   // ---------------- registers ----------------
-  const int rg = wave & 3;
   const int cg = wave >> 2;
+  const int rg = (wave + cg) & 3;
   const int frow = lane & 15;
   const int fq = lane >> 4;
   const int col_base = cg * 96;
