@@ -43,7 +43,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Offsets are formed in 32-bit buffer descriptors: keep one tile's span of
 // an operand below 2^31 bytes, and a scale array below 2^32 bytes.
 constexpr int64_t kMaxLd = int64_t(1) << 22;
-constexpr int64_t kMaxScales = int64_t(1) << 30;
+constexpr int64_t kMaxScales = int64_t(1) << 30;   // exclusive: 4 * count must fit in 32 bits
 // Every workgroup of a grouped kernel scans the E offsets to find its expert,
 // and the grouped grids grow with E: cap E so that a call stays a bounded
 // amount of work.
@@ -207,8 +207,8 @@ fp8mm_status fp8_scaled_mm(const uint8_t* A, int64_t M, int64_t K, int64_t lda, 
     return fail(FP8MM_EINVAL, "%s needs N %% 128 == 0 (N=%lld)", rule->name, (long long)N);
   if (lda < K || lda % 16 != 0 || lda > kMaxLd) return fail(FP8MM_EINVAL, "lda (%lld) must be >= K, a multiple of 16 and <= 2^22", (long long)lda);
   // the kernels address each scale array through one 32-bit buffer range
-  if (blockwise && ((K / 128) * M > kMaxScales || (K / 128) * N > kMaxScales))
-    return fail(FP8MM_EINVAL, "scale arrays of (K/128) x M or (K/128) x N above 2^30 elements are not supported");
+  if (blockwise && ((K / 128) * M >= kMaxScales || (K / 128) * N >= kMaxScales))
+    return fail(FP8MM_EINVAL, "scale arrays of (K/128) x M or (K/128) x N of 2^30 elements or more are not supported");
   const int64_t b_width = b_layout == FP8MM_B_NK ? K : N;
   if (ldb < b_width || ldb % 16 != 0 || ldb > kMaxLd)
     return fail(FP8MM_EINVAL, "ldb (%lld) must be >= %lld, a multiple of 16 and <= 2^22", (long long)ldb, (long long)b_width);
@@ -306,8 +306,8 @@ fp8mm_status fp8_scaled_grouped_mm_v2(const uint8_t* A, int64_t M_total, int64_t
   if (epi == fp8mm::Epi::Block128x128 && (K % 128 != 0 || N % 128 != 0))
     return fail(FP8MM_EINVAL, "1x128 x 128x128 needs K %% 128 == 0 and N %% 128 == 0 (K=%lld N=%lld)", (long long)K,
                 (long long)N);
-  if (epi == fp8mm::Epi::Block128x128 && (K / 128) * M_total > kMaxScales)
-    return fail(FP8MM_EINVAL, "scale_a of (K/128) x M_total above 2^30 elements is not supported");
+  if (epi == fp8mm::Epi::Block128x128 && (K / 128) * M_total >= kMaxScales)
+    return fail(FP8MM_EINVAL, "scale_a of (K/128) x M_total of 2^30 elements or more is not supported");
   if (b_layout == FP8MM_B_KN) {
     if (N % 16 != 0 || N > kMaxLd) return fail(FP8MM_EINVAL, "B stored [K, N] needs N %% 16 == 0 and N <= 2^22");
     if (K * N > (int64_t(1) << 31)) return fail(FP8MM_EINVAL, "each expert's B stored [K, N] must span fewer than 2^31 bytes");
@@ -401,8 +401,8 @@ fp8mm_status fp8_grouped_linear_grad_weight(const uint8_t* gt_q, int64_t N_out, 
   if (ld < 128 * runs || ld % 16 != 0 || ld > kMaxLd)
     return fail(FP8MM_EINVAL, "ld (%lld) must be >= 128 (T/128 + E) = %lld, a multiple of 16 and <= 2^22",
                 (long long)ld, (long long)(128 * runs));
-  if ((ld / 128) * N_out > kMaxScales || (ld / 128) * K_in > kMaxScales)
-    return fail(FP8MM_EINVAL, "scale arrays of (ld/128) x N_out or (ld/128) x K_in above 2^30 elements are not supported");
+  if ((ld / 128) * N_out >= kMaxScales || (ld / 128) * K_in >= kMaxScales)
+    return fail(FP8MM_EINVAL, "scale arrays of (ld/128) x N_out or (ld/128) x K_in of 2^30 elements or more are not supported");
   if (N_out == 0 || K_in == 0 || E == 0) return ok();
   const int64_t tiles = ((N_out + 127) / 128) * ((K_in + 127) / 128) * E;
   if (tiles > (int64_t(1) << 31) - 8) return fail(FP8MM_EINVAL, "too many output tiles");

@@ -87,6 +87,17 @@ def test_scaled_mm_rejects_before_launch(lib, kw, code):
     assert lib.fp8mm_last_error().decode()
 
 
+@pytest.mark.parametrize("kw", [
+    dict(ra=2, rb=3, M=2 ** 30, N=128, ldo=128, K=128, lda=128, ldb=128),        # 1x128 scales: (K/128) M
+    dict(ra=2, rb=4, N=2 ** 30, ldo=2 ** 30, K=128, lda=128, ldb=128),           # 128x1 scales: (K/128) N
+])
+def test_scale_arrays_of_exactly_2_30_elements_are_rejected(lib, kw):
+    # each scale array is addressed through one 32-bit byte range: 4 x 2^30
+    # bytes do not fit, so the limit is exclusive
+    assert _mm(lib, **kw) == _lib.EINVAL
+    assert "2^30" in lib.fp8mm_last_error().decode()
+
+
 def test_status_maps_to_python_exceptions(lib):
     assert _mm(lib, ra=1, rb=0) == _lib.ENOTIMPL
     with pytest.raises(NotImplementedError):
