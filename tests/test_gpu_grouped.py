@@ -102,6 +102,44 @@ def test_grouped_blockwise_more_than_64_experts(layout):
     _assert_close(got, ref, f"grouped blockwise E=70, long experts, {layout}")
 
 
+@pytest.mark.parametrize("K", [128, 32])
+def test_grouped_rowwise_at_the_expert_limit(K):
+    """E = 2^16, the most experts a grouped call accepts: every workgroup's
+    offset scan runs over 1024 chunks of 64 experts.  About 300 random
+    experts own 1-40 rows each, expert 0 five, expert 2^15 seven hundred (three
+    m-blocks) and the last expert 33; the rest are empty.  K = 128 runs on the
+    weight-streaming kernel, K = 32 (rows below its 128-byte loads) on the
+    128 x 128 grouped tiles.  Only the owning experts' weights are read, so
+    the others are zero; the oracle quantizes the owning experts' weight rows
+    (rowwise scaling is per row)."""
+    E, N = 1 << 16, 16
+    g = workloads.streams(65536 + K, 4)
+    sizes = np.zeros(E, np.int64)
+    picked = g[0].choice(np.arange(1, E - 1), 300, replace=False)
+    sizes[picked] = g[0].integers(1, 41, size=300)
+    sizes[0], sizes[E // 2], sizes[E - 1] = 5, 700, 33
+    owners = np.flatnonzero(sizes)
+    M = int(sizes.sum())
+    act = workloads.normal_bf16(g[1], (M, K))
+    w_own = workloads.normal_bf16(g[2], (owners.size, N, K), 0.02)
+    W = np.zeros((E, N, K), np.uint16)
+    W[owners] = w_own
+    offs = np.cumsum(sizes).astype(np.int32)
+    say(f"grouped rowwise E={E} N={N} K={K} M_total={M}, {owners.size} experts with rows")
+    qa, sa = fp8mm.fp8_quantize_rowwise(bf16_dev(act))
+    qw, sw = fp8mm.fp8_quantize_rowwise(bf16_dev(W.reshape(E * N, K)))
+    out = fp8mm.fp8_scaled_grouped_mm(qa, qw.reshape(E, N, K), _offs_dev(offs), sa, sw.reshape(E, N))
+    ra, rsa = quant.quantize_rowwise(act)
+    rq_own, rs_own = quant.quantize_rowwise(w_own.reshape(-1, K))
+    rw = np.zeros((E, N, K), np.uint8)
+    rw[owners] = rq_own.reshape(owners.size, N, K)
+    rsw = np.ones((E, N), np.float32)
+    rsw[owners] = rs_own.reshape(owners.size, N)
+    ref, written = gemm.grouped_mm(ra, rw, offs, rsa, rsw, out_dtype=None)
+    assert written.all()
+    _assert_close(out_f64(out), ref, f"grouped rowwise E=2^16 K={K}")
+
+
 def test_grouped_weight_gradient_more_than_64_experts():
     sizes = _many_experts_sizes()
     got, ref = _grouped_grad_weight_case(sizes, 128, 256, seed=152, out_dtype=torch.float32)
